@@ -1,0 +1,175 @@
+"""Oracle for the MoE expert-parallel local path (dispatch / combine pair).
+
+Test infrastructure: only the tests, the smoke check and the benchmark's CPU
+baseline use this module. It shares no code with the HIP path.
+
+Source: "NPU Training Operators - MC2", section "执行路径" (execution path of
+``ep_mc2_forward``): token counts by ``torch.histc(selected_experts, bins=E,
+min=0, max=E)``; ``send_counts`` = local counts and ``recv_counts`` = the
+columns of this rank's experts in the gathered counts; ``permute(hidden,
+selected_experts)``; AllToAllv + GroupedMatmul(fc1); SwiGLU; GroupedMatmul(fc2)
++ AllToAllv with the counts swapped; ``unpermute(h, unpermute_indices,
+probs=routing_weights)``. Section "迁移检查" (pre-migration checks): the local
+expert range starts at ``ep_rank * num_local_experts`` and ids must lie in
+[0, num_experts).
+
+Readings where the page is silent (each listed with the design notes):
+
+* ids outside [0, E) are invalid: counts ignore them, permute leaves them out
+  (their unpermute index is -1) and unpermute skips them;
+* the order inside one expert's segment is the flat slot order t*K + k
+  (a stable sort), which fixes every index bit-exactly;
+* ``gate_up_proj`` holds the gate in columns [0, I) and the up projection in
+  columns [I, 2I); SwiGLU(g, u) = silu(g) * u with silu(g) = g / (1 + e^-g),
+  applied to the unrounded fc1 product; the fc1 and fc2 outputs are stored as
+  bf16;
+* with a single source rank the received rows of local expert g are the send
+  buffer's rows of expert ep_rank * E_l + g, and the combine writes its result
+  back over those same rows.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .numerics import decode, round_to
+
+
+def histc(sel, num_experts: int) -> np.ndarray:
+    """counts[e] = number of (t, k) slots routed to expert e, 0 <= e < E."""
+    flat = np.asarray(sel).reshape(-1)
+    return np.array([np.count_nonzero(flat == e) for e in range(num_experts)],
+                    dtype=np.int64)
+
+
+def permute(x, sel, num_experts: int):
+    """Sort the T*K routed slots by expert, stably.
+
+    Returns ``permuted`` (rows of x in slot order, only the first n_valid rows
+    defined, as the stored bit patterns), ``sorted_idx`` (T*K: the flat slot
+    t*K+k at each position, -1 past n_valid), ``unpermute_idx`` (T*K: the
+    position of each slot, -1 for invalid ids) and ``offsets`` (E+1: start of
+    each expert's segment, offsets[E] = n_valid).
+    """
+    sel = np.asarray(sel)
+    T, K = sel.shape
+    flat = sel.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < num_experts)
+    keys = np.where(valid, flat, num_experts)
+    order = np.argsort(keys, kind="stable")
+    n_valid = int(valid.sum())
+    sorted_idx = np.full(T * K, -1, dtype=np.int64)
+    sorted_idx[:n_valid] = order[:n_valid]
+    unpermute_idx = np.full(T * K, -1, dtype=np.int64)
+    unpermute_idx[order[:n_valid]] = np.arange(n_valid)
+    counts = histc(sel, num_experts)
+    offsets = np.zeros(num_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    x = np.asarray(x)
+    permuted = x[order[:n_valid] // K]
+    return {"permuted": permuted, "sorted_idx": sorted_idx,
+            "unpermute_idx": unpermute_idx, "offsets": offsets,
+            "n_valid": n_valid}
+
+
+def silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def swiglu(a: np.ndarray) -> np.ndarray:
+    """(rows, 2I) -> (rows, I): silu(gate) * up with gate = a[:, :I]."""
+    inter = a.shape[1] // 2
+    with np.errstate(over="ignore"):
+        return silu(a[:, :inter]) * a[:, inter:]
+
+
+def gmm(rows, group_sizes, weights, *, act="none", dtype="bf16"):
+    """Grouped matmul: group g takes the next group_sizes[g] rows and
+    multiplies them by weights[g] (K, N); with ``act='swiglu'`` SwiGLU is
+    applied to the float64 product. Output rounded to ``dtype`` once."""
+    R = decode(rows, dtype)
+    Wt = decode(weights, dtype)
+    sizes = [int(s) for s in group_sizes]
+    n_out = Wt.shape[2] // 2 if act == "swiglu" else Wt.shape[2]
+    out = np.zeros((sum(sizes), n_out))
+    off = 0
+    for g, cnt in enumerate(sizes):
+        a = R[off:off + cnt] @ Wt[g]
+        out[off:off + cnt] = swiglu(a) if act == "swiglu" else a
+        off += cnt
+    return round_to(out, dtype)
+
+
+def local_slice(send_counts, ep_rank: int, local_experts: int):
+    """Rows of the send buffer that hold this rank's experts."""
+    sc = np.asarray(send_counts, dtype=np.int64)
+    start = int(sc[:ep_rank * local_experts].sum())
+    n = int(sc[ep_rank * local_experts:(ep_rank + 1) * local_experts].sum())
+    return start, n
+
+
+def check_counts(send_counts, recv_counts, ep_rank, local_experts):
+    """With one source rank, recv_counts must equal the send counts of this
+    rank's experts (the shape check of the validation table)."""
+    sc = np.asarray(send_counts, dtype=np.int64)
+    rc = np.asarray(recv_counts, dtype=np.int64)
+    mine = sc[ep_rank * local_experts:(ep_rank + 1) * local_experts]
+    if rc.shape != mine.shape or not np.array_equal(rc, mine):
+        raise ValueError("recv_counts disagree with send_counts")
+
+
+def dispatch(send_buf, send_counts, recv_counts, *, ep_rank, local_experts,
+             w1, act="swiglu"):
+    """GroupedMatmul (fc1) over the rows received for the local experts."""
+    check_counts(send_counts, recv_counts, ep_rank, local_experts)
+    start, n = local_slice(send_counts, ep_rank, local_experts)
+    rows = np.asarray(send_buf)[start:start + n]
+    return gmm(rows, recv_counts, w1, act=act)
+
+
+def combine(h_values, recv_counts, send_counts, *, ep_rank, local_experts, w2,
+            combine_buf):
+    """GroupedMatmul (fc2); the result goes back over this rank's rows of the
+    combine buffer (float64 values). ``h_values`` are the bf16 fc1 outputs."""
+    check_counts(send_counts, recv_counts, ep_rank, local_experts)
+    start, n = local_slice(send_counts, ep_rank, local_experts)
+    Wt = decode(w2, "bf16")
+    out = np.array(combine_buf, dtype=np.float64, copy=True)
+    off = 0
+    for g, cnt in enumerate(np.asarray(recv_counts, dtype=np.int64)):
+        cnt = int(cnt)
+        out[start + off:start + off + cnt] = round_to(h_values[off:off + cnt] @ Wt[g], "bf16")
+        off += cnt
+    return out
+
+
+def unpermute(y_full, unpermute_idx, probs, T: int, K: int):
+    """out[t] = sum over k of probs[t, k] * y_full[unpermute_idx[t*K + k]],
+    slots with index -1 skipped; rounded to bf16."""
+    Y = np.asarray(y_full, dtype=np.float64)
+    idx = np.asarray(unpermute_idx, dtype=np.int64).reshape(T, K)
+    P = np.asarray(probs, dtype=np.float32).astype(np.float64).reshape(T, K)
+    out = np.zeros((T, Y.shape[1]))
+    for k in range(K):
+        ok = idx[:, k] >= 0
+        out[ok] += P[ok, k][:, None] * Y[idx[ok, k]]
+    return round_to(out, "bf16")
+
+
+def moe_local(x, sel, probs, w1, w2, *, num_experts, ep_rank, local_experts,
+              combine_rest=None):
+    """The whole local path: histc -> permute -> fc1+SwiGLU -> fc2 ->
+    unpermute. ``combine_rest`` holds the float64 values of the combine-buffer
+    rows that other ranks would return (zeros when None)."""
+    sel = np.asarray(sel)
+    T, K = sel.shape
+    counts = histc(sel, num_experts)
+    p = permute(x, sel, num_experts)
+    recv = counts[ep_rank * local_experts:(ep_rank + 1) * local_experts]
+    h = dispatch(p["permuted"], counts, recv, ep_rank=ep_rank,
+                 local_experts=local_experts, w1=w1, act="swiglu")
+    H = np.asarray(x).shape[1]
+    buf = np.zeros((T * K, H)) if combine_rest is None else np.asarray(combine_rest, dtype=np.float64)
+    y_full = combine(h, recv, counts, ep_rank=ep_rank, local_experts=local_experts,
+                     w2=w2, combine_buf=buf)
+    out = unpermute(y_full, p["unpermute_idx"], probs, T, K)
+    return {"counts": counts, "permute": p, "h": h, "y_full": y_full, "out": out}

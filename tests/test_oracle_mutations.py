@@ -1,0 +1,107 @@
+"""Planted mistakes in the oracle (CPU only): each plausible slip must make at
+least one pin fail. The mistakes are planted by monkeypatching the oracle in
+this process; the oracle's source is never changed."""
+import numpy as np
+import pytest
+
+import test_oracle as pins
+from conftest import load_golden
+from oracle import gemm, moe, numerics
+
+
+def _fails(fn, *args):
+    with pytest.raises(AssertionError):
+        fn(*args)
+
+
+def test_bias_added_once_is_caught(monkeypatch):
+    real = gemm.mm_rs
+
+    def once(x1, x2, **kw):
+        b = kw.pop("bias", None)
+        out = real(x1, x2, **{**kw, "out_dtype": "f32"})
+        if b is not None:
+            out = out + numerics.decode(b, kw["in_dtype"])[None, :]
+        return numerics.round_to(out, kw.get("out_dtype") or kw["in_dtype"])
+    monkeypatch.setattr(gemm, "mm_rs", once)
+    _fails(pins.test_mm_rs_hand_example, load_golden)
+
+
+def test_transposed_operand_is_caught(monkeypatch):
+    real = gemm.ag_mm
+    monkeypatch.setattr(gemm, "ag_mm", lambda x, w, **kw: real(x, np.ascontiguousarray(np.asarray(w)[::-1]), **kw))
+    _fails(pins.test_mm_brute_force_nonsquare)
+
+
+def test_round_half_up_is_caught(monkeypatch):
+    def half_up(x, dtype):
+        x = np.asarray(x, np.float64)
+        if dtype == "f32":
+            return x
+        p, emin, fmax = numerics._FORMATS[dtype]
+        _, e = np.frexp(x)
+        ulp = np.ldexp(1.0, np.maximum(e, emin) - p)
+        q = np.floor(x / ulp + 0.5) * ulp
+        return np.where(np.abs(q) > fmax, np.copysign(np.inf, x), q)
+    monkeypatch.setattr(numerics, "round_to", half_up)
+    _fails(pins.test_round_hand_cases)
+
+
+def test_swapped_scale_index_is_caught(monkeypatch):
+    real = gemm.mm_rs
+
+    def swapped(x1, x2, **kw):
+        if kw.get("x1_scale") is not None and kw.get("x2_scale") is not None:
+            s1, s2 = kw["x1_scale"], kw["x2_scale"]
+            if np.size(s1) == np.size(s2):
+                kw = {**kw, "x1_scale": s2, "x2_scale": s1}
+        return real(x1, x2, **kw)
+    monkeypatch.setattr(gemm, "mm_rs", swapped)
+    _fails(pins.test_quant_hand_example, load_golden)
+
+
+def test_unstable_segment_order_is_caught(monkeypatch):
+    real = moe.permute
+
+    def reversed_segments(x, sel, E):
+        p = real(x, sel, E)
+        s = p["sorted_idx"].copy()
+        for e in range(E):
+            a, b = p["offsets"][e], p["offsets"][e + 1]
+            s[a:b] = s[a:b][::-1]
+        p["sorted_idx"] = s
+        return p
+    monkeypatch.setattr(moe, "permute", reversed_segments)
+    _fails(pins.test_permute_brute_force_and_properties)
+
+
+def test_swapped_gate_up_is_caught(monkeypatch):
+    monkeypatch.setattr(moe, "swiglu", lambda a: moe.silu(a[:, a.shape[1] // 2:]) * a[:, :a.shape[1] // 2])
+    _fails(pins.test_gmm_swiglu_hand_example, load_golden)
+
+
+def test_unpermute_with_wrong_index_is_caught(monkeypatch):
+    real = moe.unpermute
+
+    def wrong(y, idx, probs, T, K):
+        return real(y, np.argsort(np.asarray(idx)), probs, T, K)
+    monkeypatch.setattr(moe, "unpermute", wrong)
+    _fails(pins.test_permute_hand_example, load_golden)
+
+
+def test_dropped_partial_is_caught(monkeypatch):
+    real = gemm.mm_rs
+
+    def first_only(x1, x2, **kw):
+        if kw.get("nsim", 1) > 1:
+            kw = {**kw, "nsim": 1}
+            x1, x2 = np.asarray(x1)[0], np.asarray(x2)[0]
+        return real(x1, x2, **kw)
+    monkeypatch.setattr(gemm, "mm_rs", first_only)
+    _fails(pins.test_sim_rs_equals_concatenated_k)
+
+
+def test_histc_off_by_one_is_caught(monkeypatch):
+    real = moe.histc
+    monkeypatch.setattr(moe, "histc", lambda sel, E: np.roll(real(sel, E), 1))
+    _fails(pins.test_histc_against_torch_histc_and_bincount)
