@@ -1,0 +1,304 @@
+"""Throughput of the MC2 compute core on one MI355X.
+
+Headline step: the AllGatherMatmul local share in bf16 -- gathered x of W=8
+chunks of (1024, 3072) = (8192, 3072) @ (3072, 3072), chunks computed in
+rank order with per-chunk ready flags -- reported as TFLOP/s of the rank-chunked
+GEMM kernel. The same JSON line carries the other hot-path rows measured the
+same way (int8 quantized MatmulReduceScatter, the MoE expert-parallel local
+path, the large AllGatherMatmul and the simulated W=8 MatmulReduceScatter),
+the roofline of the dominant kernel and the CPU oracle timed on a bounded
+sample of the headline workload.
+
+Inputs are seeded synthetic data resident in HBM before timing starts. Times
+come from HIP events on the stream the kernels are launched on.
+
+    python bench.py [--steps K] [--warmup W] [--only c2|c3|c4|c5a|c5b|all]
+                    [--no-cpu-baseline] [--calib-copy]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TFLOP/s and % of MFMA peak, rank-chunked GEMM/GMM on 1 MI355X"
+PEAK_BF16 = 2500.0   # TFLOP/s, dense bf16/fp16 MFMA (published)
+PEAK_I8 = 5000.0     # TOP/s, dense int8 MFMA (published)
+PEAK_HBM = 8000.0    # GB/s, HBM3E (published)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--only", default="all")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calib-copy", action="store_true",
+                   help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's share of the work; runs on more than one GPU are "
+              "not part of this build (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as wl
+    from gemm_collective_core_amd import mc2
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def to_dev(a, bf16=False):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    def timed(fn, iters, warmup):
+        """Mean milliseconds per call of fn() over `iters` calls, HIP events on
+        the current stream (the stream every entry point launches on)."""
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(iters):
+            fn()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / iters
+
+    if args.calib_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        ms = timed(lambda: b.copy_(a), 20, 3)
+        log(f"copy 1 GiB: {ms:.3f} ms -> {2 * n / ms / 1e6:.1f} GB/s (read+write)")
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n,
+                          "ms": ms, "GBps": 2 * n / ms / 1e6}))
+        return
+
+    only = args.only
+    rows = {}
+    headline = None
+
+    # ---------------------------------------------------------------- C2
+    if only in ("all", "c2"):
+        log("C2: generating inputs")
+        d = wl.c2_inputs()
+        x, w = to_dev(d["x1"], True), to_dev(d["x2"], True)
+        W = 8
+        out = torch.empty((8192, 3072), dtype=torch.bfloat16, device=dev)
+        flags = torch.zeros(W, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(W, dtype=torch.int32, device=dev)
+        ep = [0]
+
+        def step():
+            ep[0] += 1
+            mc2.mc2_ag_mm_local(x, w, W, 0, out=out, ready_flags=flags, flag_counters=cnt,
+                                epoch=ep[0])
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for _ in range(args.steps):
+            step()
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = start.elapsed_time(end) / args.steps
+        assert flags.cpu().tolist() == [ep[0]] * W
+        flop = 2.0 * 8192 * 3072 * 3072
+        tf = flop / ms / 1e9
+        headline = {"ms": ms, "tflops": tf, "wall_s": wall, "flop": flop}
+        rows["c2_ag_mm_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+        log(f"C2 AG-MM bf16: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s  ({100 * tf / PEAK_BF16:.1f}% of peak)")
+        del x, w, out
+
+    # ---------------------------------------------------------------- C3
+    if only in ("all", "c3"):
+        log("C3: generating inputs")
+        d = wl.c3_inputs()
+        x1, x2 = to_dev(d["x1"]), to_dev(d["x2"])
+        s1, s2 = to_dev(d["x1_scale"]), to_dev(d["x2_scale"])
+        out = torch.empty((4096, 2048), dtype=torch.bfloat16, device=dev)
+        flags = torch.zeros(4, dtype=torch.int32, device=dev)
+        cnt = torch.zeros(4, dtype=torch.int32, device=dev)
+        ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, 4, 0, x1_scale=s1, x2_scale=s2, out=out,
+                                               ready_flags=flags, flag_counters=cnt, epoch=1),
+                   1000, 50)
+        top = 2.0 * 4096 * 8192 * 2048 / ms / 1e9
+        rows["c3_mm_rs_int8"] = {"ms": ms, "TOP/s": top, "frac_peak": top / PEAK_I8}
+        log(f"C3 int8 MM-RS: {ms * 1e3:.1f} us  {top:.1f} TOP/s  ({100 * top / PEAK_I8:.1f}% of peak)")
+        del x1, x2, out
+
+    # ---------------------------------------------------------------- C4
+    if only in ("all", "c4"):
+        log("C4: generating inputs")
+        d = wl.c4_inputs()
+        T, K, E, E_l, H, I = d["T"], d["K"], d["E"], d["E_l"], d["H"], d["I"]
+        x, sel, probs = to_dev(d["x"], True), to_dev(d["sel"]), to_dev(d["probs"])
+        w1, w2 = to_dev(d["w1"], True), to_dev(d["w2"], True)
+        counts = torch.empty(E, dtype=torch.int32, device=dev)
+        perm = torch.empty((T * K, H), dtype=torch.bfloat16, device=dev)
+        sidx = torch.empty(T * K, dtype=torch.int32, device=dev)
+        uidx = torch.empty(T * K, dtype=torch.int32, device=dev)
+        offs = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        ws = torch.empty(mc2.mc2_moe_permute_workspace_size(T, K, E), dtype=torch.uint8, device=dev)
+        h = torch.empty((T * K, I), dtype=torch.bfloat16, device=dev)
+        buf = torch.zeros((T * K, H), dtype=torch.bfloat16, device=dev)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        recv = counts[:E_l]
+
+        def f_histc():
+            mc2.mc2_moe_histc(sel, E, counts=counts, dev_err=err)
+
+        def f_perm():
+            mc2.mc2_moe_permute(x, sel, E, permuted=perm, sorted_idx=sidx, unpermute_idx=uidx,
+                                expert_offsets=offs, workspace=ws, dev_err=err)
+
+        def f_disp():
+            mc2.mc2_gmm_dispatch(perm, counts, recv, w1, ep_rank=0, num_experts=E, h_out=h,
+                                 dev_err=err)
+
+        def f_comb():
+            mc2.mc2_gmm_combine(h, recv, counts, w2, buf, ep_rank=0, num_experts=E, dev_err=err)
+
+        def f_unperm():
+            mc2.mc2_moe_unpermute(buf, uidx, probs, out=y, dev_err=err)
+
+        for f in (f_histc, f_perm, f_disp, f_comb, f_unperm):
+            f()
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        n_loc = int(counts[:E_l].sum().item())
+        t_h = timed(f_histc, 500, 20)
+        t_p = timed(f_perm, 200, 10)
+        t_d = timed(f_disp, 200, 10)
+        t_c = timed(f_comb, 200, 10)
+        t_u = timed(f_unperm, 200, 10)
+        t_all = timed(lambda: [f() for f in (f_histc, f_perm, f_disp, f_comb, f_unperm)], 100, 5)
+        gmm_flop = 2.0 * n_loc * H * 2 * I + 2.0 * n_loc * I * H
+        perm_bytes = T * H * 2 + T * K * 4 + T * K * H * 2 + 2 * T * K * 4
+        unperm_bytes = T * K * H * 2 + T * K * 4 + T * K * 4 + T * H * 2
+        gmm_tf = gmm_flop / (t_d + t_c) / 1e9
+        rows["c4_moe_ep_local"] = {
+            "n_loc": n_loc, "ms_step": t_all,
+            "histc_us": t_h * 1e3,
+            "permute_us": t_p * 1e3, "permute_GB/s": perm_bytes / t_p / 1e6,
+            "permute_frac_hbm": perm_bytes / t_p / 1e6 / PEAK_HBM,
+            "gmm_fc1_swiglu_us": t_d * 1e3, "gmm_fc2_us": t_c * 1e3,
+            "gmm_TFLOP/s": gmm_tf, "gmm_frac_peak": gmm_tf / PEAK_BF16,
+            "fc1_TFLOP/s": 2.0 * n_loc * H * 2 * I / t_d / 1e9,
+            "fc2_TFLOP/s": 2.0 * n_loc * I * H / t_c / 1e9,
+            "unpermute_us": t_u * 1e3, "unpermute_GB/s": unperm_bytes / t_u / 1e6,
+            "unpermute_frac_hbm": unperm_bytes / t_u / 1e6 / PEAK_HBM,
+        }
+        log("C4 MoE:", json.dumps(rows["c4_moe_ep_local"]))
+        del x, perm, h, buf, y, w1, w2
+
+    # ---------------------------------------------------------------- C5
+    if only in ("all", "c5a", "c5b"):
+        log("C5: generating inputs")
+        a, b = wl.c5_inputs()
+        W = 8
+        if only in ("all", "c5a"):
+            x, w = to_dev(a["x1"], True), to_dev(a["x2"], True)
+            out = torch.empty((16384, 3584), dtype=torch.bfloat16, device=dev)
+            flags = torch.zeros(W, dtype=torch.int32, device=dev)
+            cnt = torch.zeros(W, dtype=torch.int32, device=dev)
+            ms = timed(lambda: mc2.mc2_ag_mm_local(x, w, W, 0, out=out, ready_flags=flags,
+                                                   flag_counters=cnt, epoch=1), 100, 10)
+            tf = 2.0 * 16384 * 8192 * 3584 / ms / 1e9
+            rows["c5a_ag_mm_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+            log(f"C5a AG-MM: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
+            del x, w, out
+        if only in ("all", "c5b"):
+            x1, x2 = to_dev(b["x1"], True), to_dev(b["x2"], True)
+            out = torch.empty((16384, 8192), dtype=torch.bfloat16, device=dev)
+            flags = torch.zeros(W, dtype=torch.int32, device=dev)
+            cnt = torch.zeros(W, dtype=torch.int32, device=dev)
+            ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, W, 0, out=out, ready_flags=flags,
+                                                   flag_counters=cnt, epoch=1), 50, 5)
+            tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
+            rows["c5b_sim_rs_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+            log(f"C5b sim-W=8 MM-RS: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
+            del x1, x2, out
+
+    # ---------------------------------------------------------------- CPU oracle
+    cpu = None
+    if headline is not None and not args.no_cpu_baseline:
+        from oracle import gemm as og
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()
+                           if i.get("user_api") == "blas"] or [1])
+        except Exception:  # pragma: no cover - informational only
+            threads = len(os.sched_getaffinity(0))
+        d = wl.c2_inputs()
+        done, t0 = 0, time.perf_counter()
+        for c in range(8):
+            og.ag_mm(d["x1"], d["x2"], world_size=8, in_dtype="bf16",
+                     rows=np.arange(c * 1024, (c + 1) * 1024))
+            done += 1
+            if time.perf_counter() - t0 > 10.0:
+                break
+        dt = time.perf_counter() - t0
+        cpu = {"value": 2.0 * 1024 * done * 3072 * 3072 / dt / 1e12, "unit": "TFLOP/s",
+               "cores": threads, "kind": "oracle",
+               "sample": f"oracle.gemm.ag_mm (float64 NumPy) on {done} of the 8 row chunks "
+                         f"(1024 x 3072 @ 3072 x 3072 each) of the headline workload, "
+                         f"{dt:.1f} s"}
+        log("CPU oracle:", json.dumps(cpu))
+
+    if headline is None:
+        print(json.dumps({"rows": rows}))
+        return
+    line = {
+        "metric": METRIC,
+        "value": headline["tflops"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": headline["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0, 0.02) bf16 inputs resident in HBM)",
+        "config": {"workload": "AllGatherMatmul local share: gathered x of W=8 chunks "
+                               "(8192, 3072) @ (3072, 3072) bf16, fp32 accumulation, chunks in "
+                               "rank order from rank 0, per-chunk ready flags",
+                   "world_size": 8, "m": 8192, "k": 3072, "n": 3072},
+        "roofline": {"bound": "mfma", "achieved": headline["tflops"], "peak": PEAK_BF16,
+                     "unit": "TFLOP/s", "frac": headline["tflops"] / PEAK_BF16,
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "rows": rows,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,556 @@
+// Rank-chunked GEMM (MatmulReduceScatter / AllGatherMatmul compute share) and
+// the grouped GEMM of the MoE dispatch/combine pair, for gfx950.
+//
+// Formulas: torch_npu.npu_mm_reduce_scatter_base API doc, "功能说明" (basic and
+// quantized MatmulReduceScatter); CANN hccl issue 158 (AllGatherMatmul);
+// "NPU Training Operators - MC2", "执行路径" (GroupedMatmul fc1 + swiglu, fc2).
+#include <type_traits>
+
+#include "../../include/mc2.h"
+#include "gemm_core.hpp"
+#include "mc2_host.hpp"
+
+namespace mc2 {
+
+// ---------------------------------------------------------------- epilogues
+
+template <Out O>
+__device__ __forceinline__ void put_out(char* p, float v) {
+  if constexpr (O == Out::BF16) *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
+  else if constexpr (O == Out::F16) *reinterpret_cast<uint16_t*>(p) = f32_to_f16_bits(v);
+  else *reinterpret_cast<float*>(p) = v;
+}
+
+template <Elem E>
+__device__ __forceinline__ float load_bias(const void* bias, int64_t j) {
+  const uint16_t b = static_cast<const uint16_t*>(bias)[j];
+  if constexpr (E == Elem::F16) return f16_bits_to_f32(b);
+  else return bf16_bits_to_f32(b);  // BF16 inputs, and the bf16 bias of int8 inputs
+}
+
+// Stage the wave's accumulators (after the elementwise epilogue) into LDS as
+// the output type, row-major with `pitch` bytes per tile row.
+template <Elem E, class TS, Out O>
+__device__ __forceinline__ void stage_linear(char* smem, int pitch,
+                                             const typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
+                                             int64_t row0, int64_t row_last, int64_t col0, int64_t n,
+                                             const void* bias, float bias_mul, const float* s1,
+                                             const float* s2) {
+  constexpr int OS = OutInfo<O>::bytes;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wrow0 = (wave / TS::WN) * TS::WTM;
+  const int wcol0 = (wave % TS::WN) * TS::WTN;
+#pragma unroll
+  for (int fn = 0; fn < TS::FN; ++fn) {
+    const int lcol = wcol0 + fn * 16 + (lane & 15);
+    int64_t gcol = col0 + lcol;
+    gcol = gcol < n ? gcol : n - 1;
+    float bv = 0.f;
+    if (bias) bv = load_bias<E>(bias, gcol);
+    float sc2 = 1.f;
+    if constexpr (E == Elem::I8 && O != Out::I32) sc2 = s2[gcol];
+#pragma unroll
+    for (int fm = 0; fm < TS::FM; ++fm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
+        char* dst = smem + lrow * pitch + lcol * OS;
+        if constexpr (E == Elem::I8) {
+          if constexpr (O == Out::I32) {
+            *reinterpret_cast<int32_t*>(dst) = acc[fm][fn][i];
+          } else {
+            int64_t grow = row0 + lrow;
+            grow = grow < row_last ? grow : row_last;
+            const float sc = s1[grow] * sc2;
+            put_out<O>(dst, sc * (static_cast<float>(acc[fm][fn][i]) + bv));
+          }
+        } else {
+          put_out<O>(dst, acc[fm][fn][i] + bias_mul * bv);
+        }
+      }
+    }
+  }
+}
+
+// SwiGLU epilogue: tile column blocks alternate gate (even) and up (odd), so
+// the fragments fn = 2p and 2p + 1 of a lane hold gate and up of the same
+// output column. h = silu(g) * u, silu(g) = g / (1 + exp(-g)), stored as bf16.
+template <class TS>
+__device__ __forceinline__ void stage_swiglu(char* smem, int pitch,
+                                             const f32x4_t (&acc)[TS::FM][TS::FN]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wrow0 = (wave / TS::WN) * TS::WTM;
+  const int wcol0 = (wave % TS::WN) * TS::WTN;
+#pragma unroll
+  for (int p = 0; p < TS::FN / 2; ++p) {
+    const int lcol = wcol0 / 2 + p * 16 + (lane & 15);
+#pragma unroll
+    for (int fm = 0; fm < TS::FM; ++fm) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
+        const float g = acc[fm][2 * p][i];
+        const float u = acc[fm][2 * p + 1][i];
+        const float h = g / (1.0f + __expf(-g)) * u;
+        *reinterpret_cast<uint16_t*>(smem + lrow * pitch + lcol * 2) = f32_to_bf16_bits(h);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- chunked GEMM
+
+struct ChunkedArgs {
+  const char* A;
+  const char* B;
+  char* out;
+  const void* bias;
+  const float* s1;
+  const float* s2;
+  int64_t m, n;
+  int64_t lda, ldb, ldo;  // bytes
+  KSpan ks;
+  int64_t mc;             // rows per chunk
+  int world, first_chunk;
+  int tiles_m, tiles_n, tiles_per_chunk;
+  float bias_mul;
+  uint32_t* flags;
+  uint32_t* counters;
+  uint32_t epoch;
+};
+
+struct PlainCols {
+  int64_t col0, last_block;
+  __device__ __forceinline__ int64_t operator()(int j) const {
+    const int64_t c = col0 + j;
+    return c < last_block ? c : last_block;
+  }
+};
+
+template <class TS, int OS>
+constexpr int chunked_smem() {
+  return (2 * TS::kStageBytes) > (TS::BM * (TS::BN * OS + 16)) ? 2 * TS::kStageBytes
+                                                                 : TS::BM * (TS::BN * OS + 16);
+}
+
+template <Elem E, bool BT, class TS, Out O>
+__global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
+  constexpr int OS = OutInfo<O>::bytes;
+  constexpr int kSmem = chunked_smem<TS, OS>();
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+
+  const int b = blockIdx.x;
+  const int seq = b / p.tiles_per_chunk;
+  const int t = b - seq * p.tiles_per_chunk;
+  int c = p.first_chunk + seq;
+  c = c >= p.world ? c - p.world : c;
+  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * TS::BM;
+  const int64_t row_end = c * p.mc + p.mc;
+  const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
+
+  typename Mma<E>::acc_t acc[TS::FM][TS::FN];
+  BDesc bd{p.B, p.ldb, p.n};
+  constexpr int CPB = 16 / ElemInfo<E>::bytes;
+  PlainCols cm{col0, p.n - CPB};
+  mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
+
+  constexpr int pitch = TS::BN * OS + 16;
+  stage_linear<E, TS, O>(smem, pitch, acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul,
+                         p.s1, p.s2);
+  __syncthreads();
+  store_staged<TS::BM>(smem, pitch, TS::BN * OS, p.out + row0 * p.ldo, p.ldo, row_end - row0,
+                       col0 * OS, p.n * OS);
+
+  if (p.flags) {
+    // Every thread's stores of this tile become visible before the tile is
+    // counted; the last tile of the chunk publishes the epoch.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1 == static_cast<uint32_t>(p.tiles_per_chunk)) {
+        __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- grouped GEMM
+
+constexpr int kMaxLocalExperts = 256;
+
+struct GroupedArgs {
+  const char* A;
+  int64_t lda;
+  const char* B;
+  int64_t ldb, b_group;   // bytes per B row, bytes per expert
+  char* out;
+  int64_t ldo;
+  int64_t K;              // contraction length
+  int64_t n_b;            // columns of B per expert
+  int64_t n_out;          // output columns
+  int64_t inter;          // SwiGLU: output columns (= n_b / 2)
+  const int32_t* send_counts;
+  const int32_t* recv_counts;
+  int ep_rank, num_experts, local_experts;
+  int combine;            // 0: rows read at the send offset; 1: rows written there
+  int64_t a_cap, o_cap;   // row capacities of the A and output buffers
+  int32_t* dev_err;
+  int ktiles;
+};
+
+struct GluCols {
+  // Tile column j (16-column blocks alternate gate / up) -> global B column,
+  // clamped to the last 16-byte block; clamped columns only feed output
+  // columns >= inter, which are never stored.
+  int64_t j0, inter, last_block;
+  __device__ __forceinline__ int64_t operator()(int j) const {
+    const int cb = j >> 4;
+    const int64_t base = (cb & 1) ? inter : 0;
+    const int64_t c = base + j0 + (cb >> 1) * 16 + (j & 15);
+    return c < last_block ? c : last_block;
+  }
+};
+
+template <class TS, bool GLU>
+constexpr int grouped_smem() {
+  return (2 * TS::kStageBytes) > (TS::BM * ((GLU ? TS::BN / 2 : TS::BN) * 2 + 16))
+             ? 2 * TS::kStageBytes
+             : TS::BM * ((GLU ? TS::BN / 2 : TS::BN) * 2 + 16);
+}
+
+template <class TS, bool GLU>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
+  constexpr int kSmem = grouped_smem<TS, GLU>();
+  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ int64_t s_gstart[kMaxLocalExperts + 1];
+  __shared__ int64_t s_tstart[kMaxLocalExperts + 1];
+  __shared__ int64_t s_base;
+  __shared__ int s_bad;
+
+  const int tid = threadIdx.x;
+  const int El = p.local_experts;
+  const int first = p.ep_rank * El;
+  constexpr int OUTC = GLU ? TS::BN / 2 : TS::BN;  // output columns per tile
+  const int64_t tiles_n = (p.n_out + OUTC - 1) / OUTC;
+
+  // Counts -> group table, computed by every workgroup from device memory.
+  if (tid == 0) { s_base = 0; s_bad = 0; }
+  __syncthreads();
+  int64_t part = 0;
+  for (int e = tid; e < first; e += kThreads) {
+    const int32_t v = p.send_counts[e];
+    if (v < 0) s_bad = 1;
+    part += v;
+  }
+  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
+  if ((tid & 63) == 0 && part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_base),
+                                         static_cast<unsigned long long>(part));
+  if (tid == 0) {
+    int64_t g = 0, tt = 0;
+    for (int e = 0; e < El; ++e) {
+      const int32_t rc = p.recv_counts[e];
+      if (rc < 0 || rc != p.send_counts[first + e]) s_bad = 1;
+      s_gstart[e] = g;
+      s_tstart[e] = tt;
+      g += rc > 0 ? rc : 0;
+      tt += ((rc > 0 ? rc : 0) + TS::BM - 1) / TS::BM * tiles_n;
+    }
+    s_gstart[El] = g;
+    s_tstart[El] = tt;
+  }
+  __syncthreads();
+  {
+    const int64_t rows = s_gstart[El];
+    const int64_t a_need = (p.combine ? 0 : s_base) + rows;
+    const int64_t o_need = (p.combine ? s_base : 0) + rows;
+    if (s_bad || a_need > p.a_cap || o_need > p.o_cap) {
+      if (tid == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
+      return;
+    }
+  }
+  const int64_t a_base = p.combine ? 0 : s_base;
+  const int64_t o_base = p.combine ? s_base : 0;
+  const int64_t total = s_tstart[El];
+
+  KSpan ks{p.K, 0, 0, p.ktiles, p.ktiles};
+  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+    int g = 0;
+    while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
+    const int64_t cnt = s_gstart[g + 1] - s_gstart[g];
+    const int64_t tiles_m = (cnt + TS::BM - 1) / TS::BM;
+    const int64_t lt = t - s_tstart[g];
+    const int64_t tm = lt % tiles_m, tn = lt / tiles_m;
+    const int64_t arow0 = a_base + s_gstart[g] + tm * TS::BM;
+    const int64_t arow_end = a_base + s_gstart[g] + cnt;
+    const int64_t orow0 = o_base + s_gstart[g] + tm * TS::BM;
+    const int64_t ocol0 = tn * OUTC;
+
+    f32x4_t acc[TS::FM][TS::FN];
+    BDesc bd{p.B + g * p.b_group, p.ldb, p.n_b};
+    if constexpr (GLU) {
+      GluCols cm{ocol0, p.inter, p.n_b - 8};
+      mainloop<Elem::BF16, false, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
+    } else {
+      PlainCols cm{ocol0, p.n_b - 8};
+      mainloop<Elem::BF16, false, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks,
+                                      acc);
+    }
+    constexpr int pitch = OUTC * 2 + 16;
+    if constexpr (GLU)
+      stage_swiglu<TS>(smem, pitch, acc);
+    else
+      stage_linear<Elem::BF16, TS, Out::BF16>(smem, pitch, acc, orow0, 0, ocol0, p.n_out, nullptr,
+                                              0.f, nullptr, nullptr);
+    __syncthreads();
+    store_staged<TS::BM>(smem, pitch, OUTC * 2, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
+                         ocol0 * 2, p.n_out * 2);
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------- host side
+
+using TileMain = TileShape<128, 256, 2, 2>;
+
+template <Elem E, bool BT, Out O>
+static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s) {
+  hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TileMain, O>), dim3(blocks), dim3(kThreads), 0, s,
+                     a);
+  return hipGetLastError();
+}
+
+template <Elem E, bool BT>
+static hipError_t launch_chunked_out(const ChunkedArgs& a, int out_dtype, int blocks,
+                                     hipStream_t s) {
+  switch (out_dtype) {
+    case MC2_BF16: return launch_chunked<E, BT, Out::BF16>(a, blocks, s);
+    case MC2_F16: return launch_chunked<E, BT, Out::F16>(a, blocks, s);
+    case MC2_F32: return launch_chunked<E, BT, Out::F32>(a, blocks, s);
+    default: return launch_chunked<E, BT, Out::I32>(a, blocks, s);
+  }
+}
+
+// Instantiated combinations: F16 -> {F16, F32}; BF16 -> {BF16, F32};
+// I8 -> {BF16, F16, F32, I32}.
+template <bool BT>
+static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArgs& a, int blocks,
+                                   hipStream_t s) {
+  if (in_dtype == MC2_F16)
+    return out_dtype == MC2_F32 ? launch_chunked<Elem::F16, BT, Out::F32>(a, blocks, s)
+                                : launch_chunked<Elem::F16, BT, Out::F16>(a, blocks, s);
+  if (in_dtype == MC2_BF16)
+    return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, Out::F32>(a, blocks, s)
+                                : launch_chunked<Elem::BF16, BT, Out::BF16>(a, blocks, s);
+  return launch_chunked_out<Elem::I8, BT>(a, out_dtype, blocks, s);
+}
+
+static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
+                       int first_chunk, int nsim, int x2_trans, int in_dtype, const void* bias,
+                       const float* s1, const float* s2, int out_dtype, void* out,
+                       uint32_t* flags, uint32_t* counters, uint32_t epoch, hipStream_t stream) {
+  const int es = in_dtype == MC2_I8 ? 1 : 2;
+  const int os = (out_dtype == MC2_F32 || out_dtype == MC2_I32) ? 4 : 2;
+  ChunkedArgs a{};
+  a.A = static_cast<const char*>(x1);
+  a.B = static_cast<const char*>(x2);
+  a.out = static_cast<char*>(out);
+  a.bias = bias;
+  a.s1 = s1;
+  a.s2 = s2;
+  a.m = m;
+  a.n = n;
+  a.lda = k * es;
+  a.ldb = (x2_trans ? k : n) * es;
+  a.ldo = n * os;
+  const int ke = kKBytes / es;
+  a.ks.k = k;
+  a.ks.a_shard = m * k * es;
+  a.ks.b_shard = k * n * es;
+  a.ks.ktiles = static_cast<int>((k + ke - 1) / ke);
+  a.ks.niters = a.ks.ktiles * nsim;
+  a.mc = m / W;
+  a.world = W;
+  a.first_chunk = first_chunk;
+  a.tiles_m = static_cast<int>((a.mc + TileMain::BM - 1) / TileMain::BM);
+  a.tiles_n = static_cast<int>((n + TileMain::BN - 1) / TileMain::BN);
+  a.tiles_per_chunk = a.tiles_m * a.tiles_n;
+  a.bias_mul = static_cast<float>(nsim);
+  a.flags = flags;
+  a.counters = counters;
+  a.epoch = epoch;
+  const int64_t blocks = static_cast<int64_t>(a.tiles_per_chunk) * W;
+  if (blocks > 0x7fffffff) return MC2_ERR_SHAPE;
+  hipError_t e = x2_trans ? dispatch_chunked<true>(in_dtype, out_dtype, a, (int)blocks, stream)
+                          : dispatch_chunked<false>(in_dtype, out_dtype, a, (int)blocks, stream);
+  return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
+}
+
+static bool valid_world(int W) { return W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32; }
+
+}  // namespace mc2
+
+using namespace mc2;
+
+extern "C" int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
+                               int world_size, int rank, int nsim, int x2_trans, int in_dtype,
+                               const void* bias, const float* x1_scale, const float* x2_scale,
+                               int out_dtype, void* out, uint32_t* ready_flags,
+                               uint32_t* flag_counters, uint32_t epoch, hipStream_t stream) {
+  if (!x1 || !x2 || !out) return MC2_ERR_NULL;
+  if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
+  if (m <= 0 || n <= 0 || m % world_size) return MC2_ERR_SHAPE;
+  if (k < 256 || k >= 65535) return MC2_ERR_SHAPE;
+  if (nsim != 1 && nsim != world_size) return MC2_ERR_SHAPE;
+  if (in_dtype != MC2_F16 && in_dtype != MC2_BF16 && in_dtype != MC2_I8) return MC2_ERR_DTYPE;
+  const bool quant = in_dtype == MC2_I8;
+  if (quant) {
+    if (nsim != 1) return MC2_ERR_UNSUPPORTED;
+    if (out_dtype == MC2_I32) {
+      if (x1_scale || x2_scale || bias) return MC2_ERR_DTYPE;
+    } else if (out_dtype == MC2_BF16 || out_dtype == MC2_F16 || out_dtype == MC2_F32) {
+      if (!x1_scale || !x2_scale) return MC2_ERR_NULL;
+    } else {
+      return MC2_ERR_DTYPE;
+    }
+    if (k % 16 || n % 16) return MC2_ERR_ALIGN;
+  } else {
+    if (out_dtype != in_dtype && out_dtype != MC2_F32) return MC2_ERR_DTYPE;
+    if (x1_scale || x2_scale) return MC2_ERR_DTYPE;
+    if (k % 8 || n % 8) return MC2_ERR_ALIGN;
+  }
+  if (!aligned16(x1) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
+  if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
+  if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+  const int first = (rank + 1) % world_size;
+  return run_chunked(x1, x2, m, k, n, world_size, first, nsim, x2_trans, in_dtype, bias, x1_scale,
+                     x2_scale, out_dtype, out, ready_flags, flag_counters, epoch, stream);
+}
+
+extern "C" int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
+                               int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
+                               const void* bias, void* out, uint32_t* ready_flags,
+                               uint32_t* flag_counters, uint32_t epoch, hipStream_t stream) {
+  if (!x_gathered || !x2 || !out) return MC2_ERR_NULL;
+  if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
+  if (m_c <= 0 || n <= 0 || k <= 0) return MC2_ERR_SHAPE;
+  if (in_dtype != MC2_F16 && in_dtype != MC2_BF16) return MC2_ERR_DTYPE;
+  if (k % 8 || n % 8) return MC2_ERR_ALIGN;
+  if (!aligned16(x_gathered) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
+  if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
+  if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+  return run_chunked(x_gathered, x2, m_c * world_size, k, n, world_size, rank, 1, x2_trans,
+                     in_dtype, bias, nullptr, nullptr, in_dtype, out, ready_flags, flag_counters,
+                     epoch, stream);
+}
+
+// ---------------------------------------------------------------- grouped entry points
+
+namespace mc2 {
+
+using TileGroup = TileShape<128, 256, 2, 2>;
+
+static int run_grouped(bool glu, const GroupedArgs& a, int64_t max_tiles, hipStream_t stream) {
+  const int64_t grid64 = max_tiles < num_cus() ? max_tiles : num_cus();
+  const int grid = static_cast<int>(grid64 > 0 ? grid64 : 1);
+  if (glu)
+    hipLaunchKernelGGL((grouped_gemm_kernel<TileGroup, true>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
+  else
+    hipLaunchKernelGGL((grouped_gemm_kernel<TileGroup, false>), dim3(grid), dim3(kThreads), 0,
+                       stream, a);
+  return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
+}
+
+static int check_ep(int world_size_src, int ep_rank, int num_experts, int local_experts) {
+  if (world_size_src != 1) return MC2_ERR_UNSUPPORTED;
+  if (num_experts < 1 || local_experts < 1 || local_experts > kMaxLocalExperts) return MC2_ERR_SHAPE;
+  if (num_experts % local_experts) return MC2_ERR_SHAPE;
+  if (ep_rank < 0 || ep_rank >= num_experts / local_experts) return MC2_ERR_SHAPE;
+  return MC2_OK;
+}
+
+}  // namespace mc2
+
+extern "C" int mc2_gmm_dispatch(const void* send_buf, int64_t send_rows, const int32_t* send_counts,
+                                const int32_t* recv_counts, int world_size_src, int ep_rank,
+                                int num_experts, int local_experts, const void* w1, int64_t H,
+                                int64_t I2, int act, void* h_out, int64_t h_rows,
+                                int32_t* dev_err, hipStream_t stream) {
+  if (!send_buf || !send_counts || !recv_counts || !w1 || !h_out) return MC2_ERR_NULL;
+  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
+  if (st) return st;
+  if (H < 1 || I2 < 16 || send_rows < 0 || h_rows < 0) return MC2_ERR_SHAPE;
+  if (act != MC2_ACT_NONE && act != MC2_ACT_SWIGLU) return MC2_ERR_SHAPE;
+  if (H % 8 || I2 % 16) return MC2_ERR_ALIGN;
+  if (!aligned16(send_buf) || !aligned16(w1) || !aligned16(h_out)) return MC2_ERR_ALIGN;
+  const bool glu = act == MC2_ACT_SWIGLU;
+  GroupedArgs a{};
+  a.A = static_cast<const char*>(send_buf);
+  a.lda = H * 2;
+  a.B = static_cast<const char*>(w1);
+  a.ldb = I2 * 2;
+  a.b_group = H * I2 * 2;
+  a.out = static_cast<char*>(h_out);
+  a.n_b = I2;
+  a.n_out = glu ? I2 / 2 : I2;
+  a.inter = I2 / 2;
+  a.ldo = a.n_out * 2;
+  a.K = H;
+  a.send_counts = send_counts;
+  a.recv_counts = recv_counts;
+  a.ep_rank = ep_rank;
+  a.num_experts = num_experts;
+  a.local_experts = local_experts;
+  a.combine = 0;
+  a.a_cap = send_rows;
+  a.o_cap = h_rows;
+  a.dev_err = dev_err;
+  a.ktiles = static_cast<int>((H + 63) / 64);
+  const int outc = glu ? TileGroup::BN / 2 : TileGroup::BN;
+  const int64_t rows = send_rows < h_rows ? send_rows : h_rows;
+  const int64_t max_tiles = (rows / TileGroup::BM + local_experts) * ((a.n_out + outc - 1) / outc);
+  return run_grouped(glu, a, max_tiles, stream);
+}
+
+extern "C" int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* recv_counts,
+                               const int32_t* send_counts, int world_size_src, int ep_rank,
+                               int num_experts, int local_experts, const void* w2, int64_t I,
+                               int64_t H, void* combine_buf, int64_t combine_rows,
+                               int32_t* dev_err, hipStream_t stream) {
+  if (!h || !send_counts || !recv_counts || !w2 || !combine_buf) return MC2_ERR_NULL;
+  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
+  if (st) return st;
+  if (I < 1 || H < 8 || h_rows < 0 || combine_rows < 0) return MC2_ERR_SHAPE;
+  if (I % 8 || H % 8) return MC2_ERR_ALIGN;
+  if (!aligned16(h) || !aligned16(w2) || !aligned16(combine_buf)) return MC2_ERR_ALIGN;
+  GroupedArgs a{};
+  a.A = static_cast<const char*>(h);
+  a.lda = I * 2;
+  a.B = static_cast<const char*>(w2);
+  a.ldb = H * 2;
+  a.b_group = I * H * 2;
+  a.out = static_cast<char*>(combine_buf);
+  a.n_b = H;
+  a.n_out = H;
+  a.inter = 0;
+  a.ldo = H * 2;
+  a.K = I;
+  a.send_counts = send_counts;
+  a.recv_counts = recv_counts;
+  a.ep_rank = ep_rank;
+  a.num_experts = num_experts;
+  a.local_experts = local_experts;
+  a.combine = 1;
+  a.a_cap = h_rows;
+  a.o_cap = combine_rows;
+  a.dev_err = dev_err;
+  a.ktiles = static_cast<int>((I + 63) / 64);
+  const int64_t rows = h_rows < combine_rows ? h_rows : combine_rows;
+  const int64_t max_tiles =
+      (rows / TileGroup::BM + local_experts) * ((H + TileGroup::BN - 1) / TileGroup::BN);
+  return run_grouped(false, a, max_tiles, stream);
+}

@@ -1,0 +1,194 @@
+"""Thin Python binding over the C ABI of ``include/mc2.h``.
+
+Every function has the name of the C entry point it calls and only marshals
+arguments: it checks that tensors live on the GPU with the expected dtype and
+layout, passes their data pointers and the current HIP stream, and raises
+:class:`Mc2Error` on a nonzero status. All computation runs in the HIP
+library; there is no other code path.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+MC2_F16, MC2_BF16, MC2_I8, MC2_F32, MC2_I32 = 0, 1, 2, 3, 4
+MC2_ACT_NONE, MC2_ACT_SWIGLU = 0, 1
+MC2_DEVERR_EXPERT_ID, MC2_DEVERR_COUNTS, MC2_DEVERR_INDEX = 1, 2, 4
+
+_CODES = {torch.float16: MC2_F16, torch.bfloat16: MC2_BF16, torch.int8: MC2_I8,
+          torch.float32: MC2_F32, torch.int32: MC2_I32}
+_TORCH = {v: k for k, v in _CODES.items()}
+
+
+class Mc2Error(RuntimeError):
+    def __init__(self, fn, status):
+        msg = _lib.load().mc2_status_string(status).decode()
+        super().__init__(f"{fn} failed: {msg}")
+        self.status = status
+
+
+def _check(fn, status):
+    if status != 0:
+        raise Mc2Error(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None:
+            if not t.is_cuda:
+                raise ValueError("tensors must be on the GPU")
+            if not t.is_contiguous():
+                raise ValueError("tensors must be contiguous")
+    return next(t for t in ts if t is not None).device
+
+
+def _stream(device):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    return _CODES[dt]
+
+
+def mc2_version() -> str:
+    return _lib.load().mc2_version().decode()
+
+
+def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_scale=None,
+                    x2_scale=None, out_dtype=None, out=None, ready_flags=None,
+                    flag_counters=None, epoch=0):
+    """MatmulReduceScatter compute share; x1 (m, k) or stacked (nsim, m, k),
+    x2 (k, n) / (n, k) or stacked. Returns out (m, n)."""
+    dev = _dev(x1, x2, bias, x1_scale, x2_scale, out, ready_flags, flag_counters)
+    nsim = 1 if x1.dim() == 2 else x1.shape[0]
+    m, k = x1.shape[-2], x1.shape[-1]
+    n = x2.shape[-2] if x2_trans else x2.shape[-1]
+    if x2.dim() != x1.dim() or (x2.dim() == 3 and x2.shape[0] != nsim):
+        raise ValueError("x1 and x2 must be stacked alike")
+    if (x2.shape[-1] if x2_trans else x2.shape[-2]) != k:
+        raise ValueError("k mismatch between x1 and x2")
+    if out_dtype is None:
+        out_dtype = torch.bfloat16 if x1.dtype == torch.int8 else x1.dtype
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    elif out.shape != (m, n) or out.dtype != out_dtype:
+        raise ValueError("out must be (m, n) of out_dtype")
+    st = _lib.load().mc2_mm_rs_local(
+        x1.data_ptr(), x2.data_ptr(), m, k, n, world_size, rank, nsim, int(bool(x2_trans)),
+        _CODES[x1.dtype], _ptr(bias), _ptr(x1_scale), _ptr(x2_scale), _CODES[out_dtype],
+        out.data_ptr(), _ptr(ready_flags), _ptr(flag_counters), epoch, _stream(dev))
+    _check("mc2_mm_rs_local", st)
+    return out
+
+
+def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=None, out=None,
+                    ready_flags=None, flag_counters=None, epoch=0):
+    """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out."""
+    dev = _dev(x_gathered, x2, bias, out, ready_flags, flag_counters)
+    M, k = x_gathered.shape
+    if M % world_size:
+        raise ValueError("rows of x_gathered must be world_size * m_c")
+    n = x2.shape[0] if x2_trans else x2.shape[1]
+    if out is None:
+        out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
+    st = _lib.load().mc2_ag_mm_local(
+        x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
+        int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
+        _ptr(ready_flags), _ptr(flag_counters), epoch, _stream(dev))
+    _check("mc2_ag_mm_local", st)
+    return out
+
+
+def mc2_moe_histc(sel, num_experts, *, counts=None, dev_err=None):
+    dev = _dev(sel, counts, dev_err)
+    if sel.dtype != torch.int32:
+        raise ValueError("sel must be int32")
+    if counts is None:
+        counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
+    st = _lib.load().mc2_moe_histc(sel.data_ptr(), sel.numel(), num_experts, counts.data_ptr(),
+                                   _ptr(dev_err), _stream(dev))
+    _check("mc2_moe_histc", st)
+    return counts
+
+
+def mc2_moe_permute_workspace_size(T, K, num_experts) -> int:
+    return int(_lib.load().mc2_moe_permute_workspace_size(T, K, num_experts))
+
+
+def mc2_moe_permute(x, sel, num_experts, *, permuted=None, sorted_idx=None, unpermute_idx=None,
+                    expert_offsets=None, workspace=None, dev_err=None):
+    """Returns (permuted, sorted_idx, unpermute_idx, expert_offsets)."""
+    dev = _dev(x, sel, permuted, sorted_idx, unpermute_idx, expert_offsets, workspace, dev_err)
+    T, H = x.shape
+    K = sel.shape[1]
+    if sel.dtype != torch.int32 or sel.shape[0] != T:
+        raise ValueError("sel must be int32 (T, K)")
+    if x.element_size() != 2:
+        raise ValueError("x must hold 16-bit elements")
+    if permuted is None:
+        permuted = torch.empty((T * K, H), dtype=x.dtype, device=dev)
+    if sorted_idx is None:
+        sorted_idx = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if unpermute_idx is None:
+        unpermute_idx = torch.empty(T * K, dtype=torch.int32, device=dev)
+    if expert_offsets is None:
+        expert_offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    ws = mc2_moe_permute_workspace_size(T, K, num_experts)
+    if workspace is None:
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=dev)
+    st = _lib.load().mc2_moe_permute(
+        x.data_ptr(), T, H, sel.data_ptr(), K, num_experts, permuted.data_ptr(),
+        sorted_idx.data_ptr(), unpermute_idx.data_ptr(), expert_offsets.data_ptr(),
+        workspace.data_ptr(), workspace.numel() * workspace.element_size(), _ptr(dev_err),
+        _stream(dev))
+    _check("mc2_moe_permute", st)
+    return permuted, sorted_idx, unpermute_idx, expert_offsets
+
+
+def mc2_gmm_dispatch(send_buf, send_counts, recv_counts, w1, *, ep_rank, num_experts,
+                     world_size_src=1, act=MC2_ACT_SWIGLU, h_out=None, dev_err=None):
+    """Grouped fc1 (+ SwiGLU) over the rows of the local experts. h_out must
+    hold at least as many rows as the local experts receive; by default it has
+    as many rows as send_buf."""
+    dev = _dev(send_buf, send_counts, recv_counts, w1, h_out, dev_err)
+    E_l, H, I2 = w1.shape
+    n_out = I2 // 2 if act == MC2_ACT_SWIGLU else I2
+    if h_out is None:
+        h_out = torch.empty((send_buf.shape[0], n_out), dtype=torch.bfloat16, device=dev)
+    st = _lib.load().mc2_gmm_dispatch(
+        send_buf.data_ptr(), send_buf.shape[0], send_counts.data_ptr(), recv_counts.data_ptr(),
+        world_size_src, ep_rank, num_experts, E_l, w1.data_ptr(), H, I2, act, h_out.data_ptr(),
+        h_out.shape[0], _ptr(dev_err), _stream(dev))
+    _check("mc2_gmm_dispatch", st)
+    return h_out
+
+
+def mc2_gmm_combine(h, recv_counts, send_counts, w2, combine_buf, *, ep_rank, num_experts,
+                    world_size_src=1, dev_err=None):
+    """Grouped fc2 written back over the local experts' rows of combine_buf."""
+    dev = _dev(h, recv_counts, send_counts, w2, combine_buf, dev_err)
+    E_l, I, H = w2.shape
+    st = _lib.load().mc2_gmm_combine(
+        h.data_ptr(), h.shape[0], recv_counts.data_ptr(), send_counts.data_ptr(), world_size_src,
+        ep_rank, num_experts, E_l, w2.data_ptr(), I, H, combine_buf.data_ptr(),
+        combine_buf.shape[0], _ptr(dev_err), _stream(dev))
+    _check("mc2_gmm_combine", st)
+    return combine_buf
+
+
+def mc2_moe_unpermute(y_full, unpermute_idx, probs, *, out=None, dev_err=None):
+    dev = _dev(y_full, unpermute_idx, probs, out, dev_err)
+    T, K = probs.shape
+    H = y_full.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    st = _lib.load().mc2_moe_unpermute(
+        y_full.data_ptr(), y_full.shape[0], unpermute_idx.data_ptr(), probs.data_ptr(), T, K, H,
+        out.data_ptr(), _ptr(dev_err), _stream(dev))
+    _check("mc2_moe_unpermute", st)
+    return out

@@ -1,0 +1,236 @@
+/*
+ * mc2.h -- C ABI of the MI355X (gfx950) compute core of the MC2 fused
+ * compute/communication operators: one GPU's share of MatmulReduceScatter,
+ * AllGatherMatmul and the MoE AllToAllv+GroupedMatmul dispatch/combine pair.
+ *
+ * Sources (page title, section):
+ *   [RS]  torch_npu.npu_mm_reduce_scatter_base API doc -- "功能说明" (formulas),
+ *         "函数原型" (prototype), "参数说明" (arguments), "返回值说明" (return).
+ *   [AG]  CANN hccl issue 158 (AllGather vs AllGather+MatMul latency on Atlas A2)
+ *         -- the benchmark script's npu_all_gather_base_mm call.
+ *   [EP]  "NPU Training Operators - MC2" -- "执行路径" (execution path of
+ *         ep_mc2_forward), "迁移检查" (pre-migration checks), "验证项"
+ *         (validation table).
+ *
+ * Conventions shared by every entry point:
+ *   - All pointers are device pointers unless stated; the caller owns every
+ *     buffer. The library allocates no device memory.
+ *   - Every call validates its arguments on the host first. On failure it
+ *     returns a nonzero mc2_status and enqueues nothing.
+ *   - On success the work is enqueued on `stream` and the call returns at once;
+ *     results are ordered on that stream. A launch failure reported by the HIP
+ *     runtime returns MC2_ERR_HIP.
+ *   - Data-dependent faults (expert ids out of range, inconsistent counts,
+ *     indices out of range) never force a host synchronisation: the kernels
+ *     OR an MC2_DEVERR_* bit into *dev_err when dev_err is not NULL, and skip
+ *     the offending data so that every access stays in bounds.
+ *   - Matrices are row-major and densely packed. Base pointers must be 16-byte
+ *     aligned. No C++ exception crosses this interface.
+ */
+#ifndef MC2_H_
+#define MC2_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mc2_status {
+  MC2_OK = 0,
+  MC2_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  MC2_ERR_SHAPE = 2,       /* a size or shape constraint is violated        */
+  MC2_ERR_DTYPE = 3,       /* a dtype or dtype combination is not allowed   */
+  MC2_ERR_UNSUPPORTED = 4, /* valid per the pages but not built here        */
+  MC2_ERR_HIP = 5,         /* the HIP runtime reported a launch error       */
+  MC2_ERR_WORKSPACE = 6,   /* workspace too small                           */
+  MC2_ERR_ALIGN = 7        /* a pointer or row pitch is not 16-byte aligned */
+} mc2_status;
+
+typedef enum mc2_dtype {
+  MC2_F16 = 0,
+  MC2_BF16 = 1,
+  MC2_I8 = 2,
+  MC2_F32 = 3, /* output only, test extension: the value before the cast  */
+  MC2_I32 = 4  /* output only, test extension: the raw int8 accumulator   */
+} mc2_dtype;
+
+typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
+
+/* Bits ORed into *dev_err by the kernels. */
+#define MC2_DEVERR_EXPERT_ID 1u /* an expert id outside [0, num_experts)      */
+#define MC2_DEVERR_COUNTS 2u    /* recv_counts disagree with send_counts, or   */
+                                /* the counted rows exceed a buffer's rows     */
+#define MC2_DEVERR_INDEX 4u     /* an unpermute index outside the y buffer     */
+
+/*
+ * mc2_mm_rs_local -- MatmulReduceScatter compute share [RS].
+ *
+ *   basic:  P = sum_{w < nsim} (x1_w @ x2_w + bias)
+ *   quant:  P = sum_{w < nsim} (x1_scale[i] * x2_scale[j]) * (x1_w @ x2_w + bias)
+ *
+ * and destination chunk c (c < world_size) is rows [c*m/W, (c+1)*m/W) of the
+ * (m, n) result `out`. nsim == 1 computes this rank's own partial (the real
+ * per-rank share); nsim == world_size sums the W stacked partials on one
+ * device (the reduce-scatter arithmetic), accumulating all W*k products in one
+ * fp32 (or int32) accumulator and rounding once.
+ *
+ *   x1      (nsim, m, k) in_dtype             x2  (nsim, k, n), or (nsim, n, k)
+ *                                                 when x2_trans != 0
+ *   in_dtype MC2_F16, MC2_BF16 or MC2_I8 (x1 and x2 share it)
+ *   bias    NULL or (n): in_dtype for F16/BF16 inputs; BF16 for I8 inputs
+ *           (an extension: the page allows only a float bias of the input's
+ *           dtype). The literal formula adds it inside every partial.
+ *   x1_scale (m) fp32 per token, x2_scale (n) fp32 per channel: required for
+ *           I8 unless out_dtype is MC2_I32; must be NULL otherwise.
+ *   out_dtype  F16/BF16 inputs: equal to in_dtype, or MC2_F32 (test).
+ *              I8 inputs: MC2_BF16 (the page's default), MC2_F16, MC2_F32
+ *              (test: the fp32 dequantised value) or MC2_I32 (test: the raw
+ *              accumulator; no scales, no bias, nsim == 1).
+ *   out     (m, n) out_dtype, written chunk by chunk.
+ *
+ * Constraints [RS "参数说明"]: m % world_size == 0; 256 <= k < 65535;
+ * world_size in {1, 2, 4, 8, 16, 32} (1 is a test extension); 0 <= rank < W;
+ * nsim in {1, world_size}, and nsim == 1 for I8. Built restrictions: k % 8 == 0
+ * (k % 16 for I8) and n % 8 == 0 (n % 16 for I8) so rows stay 16-byte aligned.
+ *
+ * Chunk schedule and ready flags: chunks are computed in the order
+ * (rank + 1 + i) mod W, i = 0..W-1, so that the chunk this rank keeps comes
+ * last. When ready_flags is not NULL, flag_counters must point to W uint32
+ * that are zero before the first call (the library leaves them zero after
+ * each call); the last tile to finish chunk c stores ready_flags[c] = epoch
+ * with release ordering at system scope once every byte of chunk c is
+ * visible. epoch must be nonzero and should differ between calls. Both flag
+ * pointers NULL disables flags.
+ */
+int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
+                    int world_size, int rank, int nsim, int x2_trans, int in_dtype,
+                    const void* bias, const float* x1_scale, const float* x2_scale,
+                    int out_dtype, void* out, uint32_t* ready_flags,
+                    uint32_t* flag_counters, uint32_t epoch, hipStream_t stream);
+
+/*
+ * mc2_ag_mm_local -- AllGatherMatmul compute share [AG]: out = allgather(x1) @ x2
+ * (+ bias).
+ *
+ *   x_gathered (W*m_c, k): the W gathered chunks, chunk c = rows of rank c.
+ *   x2 (k, n), or (n, k) when x2_trans != 0; bias NULL or (n); all in_dtype
+ *   (MC2_F16 or MC2_BF16). out (W*m_c, n) in_dtype.
+ *
+ * Chunks are computed in the order (rank + i) mod W, starting with the chunk
+ * this rank owns. Ready flags as for mc2_mm_rs_local. Constraints: k >= 1,
+ * k % 8 == 0, n % 8 == 0, m_c >= 1, world_size in {1, 2, 4, 8, 16, 32}.
+ */
+int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
+                    int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
+                    const void* bias, void* out, uint32_t* ready_flags,
+                    uint32_t* flag_counters, uint32_t epoch, hipStream_t stream);
+
+/*
+ * mc2_moe_histc -- token count per expert [EP "执行路径": torch.histc with
+ * bins = num_experts, min = 0, max = num_experts]:
+ *   counts[e] = #{ i < n_ids : sel[i] == e },  0 <= e < num_experts.
+ * Ids outside [0, num_experts) are not counted and set MC2_DEVERR_EXPERT_ID.
+ * sel (n_ids) int32; counts (num_experts) int32, fully overwritten.
+ * Constraints: n_ids >= 0, 1 <= num_experts <= 1024.
+ */
+int mc2_moe_histc(const int32_t* sel, int64_t n_ids, int num_experts, int32_t* counts,
+                  int32_t* dev_err, hipStream_t stream);
+
+/* Workspace bytes that mc2_moe_permute needs for T tokens, K slots, E experts. */
+size_t mc2_moe_permute_workspace_size(int64_t T, int K, int num_experts);
+
+/*
+ * mc2_moe_permute -- stable grouping of the T*K routed slots by expert
+ * [EP "执行路径": permute(hidden_states, selected_experts)].
+ *
+ * Slot s = t*K + k routes token t to expert sel[s]. Slots are sorted by expert,
+ * ties kept in slot order. With n_valid slots whose ids lie in [0, E):
+ *   sorted_idx[p]      = slot at position p (p < n_valid), -1 for p >= n_valid
+ *   unpermute_idx[s]   = position of slot s, -1 if sel[s] is out of range
+ *   expert_offsets[e]  = first position of expert e; expert_offsets[E] = n_valid
+ *   permuted[p]        = x[sorted_idx[p] / K]  (a byte copy of the row)
+ * x (T, H) and permuted (T*K, H) hold 16-bit elements (bf16 or fp16); rows
+ * p >= n_valid of permuted are not written. workspace: at least
+ * mc2_moe_permute_workspace_size(T, K, E) bytes, 16-byte aligned, contents
+ * need not be initialised. Constraints: T >= 1, 1 <= K <= 64,
+ * 1 <= E <= 1024, H % 8 == 0, T*K < 2^31.
+ */
+int mc2_moe_permute(const void* x, int64_t T, int64_t H, const int32_t* sel, int K,
+                    int num_experts, void* permuted, int32_t* sorted_idx,
+                    int32_t* unpermute_idx, int32_t* expert_offsets, void* workspace,
+                    size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
+
+/*
+ * mc2_gmm_dispatch -- GroupedMatmul part of the dispatch segment
+ * [EP "执行路径": AllToAllv -> GroupedMatmul(fc1), then swiglu].
+ *
+ * This rank (ep_rank) owns experts [ep_rank*E_l, (ep_rank+1)*E_l) of
+ * num_experts; send_counts (num_experts) are the per-expert row counts of the
+ * permuted send buffer and recv_counts (world_size_src * E_l, source-rank
+ * major) the rows received per (source rank, local expert). With one source
+ * rank (world_size_src == 1, the only value built here) the received rows of
+ * local expert g are the send buffer's rows of expert ep_rank*E_l + g, and
+ * recv_counts must equal those send counts (else MC2_DEVERR_COUNTS and nothing
+ * is computed). For each local expert g, on its rows R_g:
+ *   act == MC2_ACT_NONE:   h = R_g @ w1[g]                      -> (rows, I2)
+ *   act == MC2_ACT_SWIGLU: a = R_g @ w1[g]; h = silu(a[:, :I2/2]) * a[:, I2/2:]
+ *                          with silu(g) = g / (1 + exp(-g))       -> (rows, I2/2)
+ * accumulated in fp32 and stored as bf16, group after group from row 0 of h_out.
+ *
+ *   send_buf (send_rows, H) bf16; w1 (E_l, H, I2) bf16 (gate columns [0, I2/2),
+ *   up columns [I2/2, I2)); h_out (h_rows, I2 or I2/2) bf16. Counts are read on
+ *   the device only. Constraints: H % 8 == 0, I2 % 16 == 0, H >= 1.
+ */
+int mc2_gmm_dispatch(const void* send_buf, int64_t send_rows, const int32_t* send_counts,
+                     const int32_t* recv_counts, int world_size_src, int ep_rank,
+                     int num_experts, int local_experts, const void* w1, int64_t H,
+                     int64_t I2, int act, void* h_out, int64_t h_rows, int32_t* dev_err,
+                     hipStream_t stream);
+
+/*
+ * mc2_gmm_combine -- GroupedMatmul part of the combine segment
+ * [EP "执行路径": GroupedMatmul(fc2) -> AllToAllv, counts swapped].
+ *
+ * For each local expert g on its rows of h (group after group from row 0):
+ * y = h_g @ w2[g] in fp32, stored as bf16 into combine_buf at the rows the
+ * send buffer used for expert ep_rank*E_l + g (with one source rank the
+ * return AllToAllv puts the rows back where they were sent from). Other rows
+ * of combine_buf are not touched. Count checks as for mc2_gmm_dispatch.
+ *
+ *   h (h_rows, I) bf16; w2 (E_l, I, H) bf16; combine_buf (combine_rows, H) bf16.
+ *   Constraints: I % 8 == 0, H % 8 == 0.
+ */
+int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* recv_counts,
+                    const int32_t* send_counts, int world_size_src, int ep_rank,
+                    int num_experts, int local_experts, const void* w2, int64_t I,
+                    int64_t H, void* combine_buf, int64_t combine_rows, int32_t* dev_err,
+                    hipStream_t stream);
+
+/*
+ * mc2_moe_unpermute -- weighted return of the routed rows to their tokens
+ * [EP "执行路径": unpermute(h, unpermute_indices, probs=routing_weights)]:
+ *   out[t] = sum_{k < K} probs[t*K + k] * y_full[unpermute_idx[t*K + k]]
+ * accumulated in fp32 in ascending k and stored as bf16. Slots with index -1
+ * are skipped; an index >= y_rows is skipped and sets MC2_DEVERR_INDEX.
+ *   y_full (y_rows, H) bf16; unpermute_idx (T*K) int32; probs (T*K) fp32;
+ *   out (T, H) bf16. Constraints: H % 8 == 0, 1 <= K <= 64.
+ */
+int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermute_idx,
+                      const float* probs, int64_t T, int K, int64_t H, void* out,
+                      int32_t* dev_err, hipStream_t stream);
+
+/* Human-readable name of an mc2_status value (static storage). */
+const char* mc2_status_string(int status);
+
+/* Library version string (static storage). */
+const char* mc2_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MC2_H_ */

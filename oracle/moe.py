@@ -155,6 +155,44 @@ def unpermute(y_full, unpermute_idx, probs, T: int, K: int):
     return round_to(out, "bf16")
 
 
+def expert_ffn_rows(x_rows, experts, w1, w2):
+    """fc1 + SwiGLU and fc2 for single rows: row i goes through local expert
+    experts[i]. Returns (h, y) as float64 values of the bf16 results."""
+    X = decode(x_rows, "bf16")
+    experts = [int(e) for e in experts]
+    W1 = {e: decode(np.asarray(w1)[e], "bf16") for e in set(experts)}
+    W2 = {e: decode(np.asarray(w2)[e], "bf16") for e in set(experts)}
+    h = np.stack([round_to(swiglu((X[i] @ W1[e])[None, :])[0], "bf16")
+                  for i, e in enumerate(experts)])
+    y = np.stack([round_to(h[i] @ W2[e], "bf16") for i, e in enumerate(experts)])
+    return h, y
+
+
+def token_outputs(x, sel, probs, w1, w2, tokens, *, ep_rank, local_experts):
+    """Unpermuted output of the given tokens when only this rank's experts
+    contribute: out[t] = bf16(sum_k probs[t,k] * y(x[t], sel[t,k])) over the
+    slots routed to a local expert, k ascending (y as in
+    :func:`expert_ffn_rows`)."""
+    sel = np.asarray(sel)
+    x = np.asarray(x)
+    first = ep_rank * local_experts
+    rows, exps, owner, wts = [], [], [], []
+    for i, t in enumerate(tokens):
+        for k in range(sel.shape[1]):
+            e = int(sel[t, k]) - first
+            if 0 <= e < local_experts:
+                rows.append(t)
+                exps.append(e)
+                owner.append(i)
+                wts.append(float(np.float32(probs[t, k])))
+    acc = np.zeros((len(tokens), x.shape[1]))
+    if rows:
+        _, y = expert_ffn_rows(x[rows], exps, w1, w2)
+        for j in range(len(rows)):
+            acc[owner[j]] += wts[j] * y[j]
+    return round_to(acc, "bf16")
+
+
 def moe_local(x, sel, probs, w1, w2, *, num_experts, ep_rank, local_experts,
               combine_rest=None):
     """The whole local path: histc -> permute -> fc1+SwiGLU -> fc2 ->

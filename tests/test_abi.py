@@ -1,0 +1,117 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/mc2.h declares, and rejects invalid arguments on the host before any
+launch (these calls fail validation, so no device work is ever enqueued)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+from gemm_collective_core_amd import _lib
+
+HEADER = os.path.join(ROOT, "include", "mc2.h")
+FAKE = 0x1000  # a non-NULL, 16-byte aligned address that is never dereferenced
+
+MC2_OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_UNSUP, ERR_HIP, ERR_WS, ERR_ALIGN = range(8)
+F16, BF16, I8, F32, I32 = range(5)
+
+
+def declared():
+    text = open(HEADER, encoding="utf-8").read()
+    return sorted(set(re.findall(r"^(?:int|size_t|const char\*)\s+(mc2_\w+)\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libmc2.so is not built: run `python -m gemm_collective_core_amd.build`")
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared()
+    assert len(names) == 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in _lib.SIGNATURES, n
+    assert set(_lib.SIGNATURES) == set(names)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.mc2_version().decode().startswith("mc2-gfx950")
+    for s in range(8):
+        assert lib.mc2_status_string(s).decode().startswith("MC2_")
+    assert b"unknown" in lib.mc2_status_string(99)
+
+
+def rs(lib, **over):
+    a = dict(x1=FAKE, x2=FAKE, m=128, k=512, n=64, W=2, rank=0, nsim=1, trans=0, dt=F16,
+             bias=None, s1=None, s2=None, odt=F16, out=FAKE, flags=None, cnt=None, epoch=0)
+    a.update(over)
+    return lib.mc2_mm_rs_local(a["x1"], a["x2"], a["m"], a["k"], a["n"], a["W"], a["rank"],
+                               a["nsim"], a["trans"], a["dt"], a["bias"], a["s1"], a["s2"],
+                               a["odt"], a["out"], a["flags"], a["cnt"], a["epoch"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x1=None), ERR_NULL),
+    (dict(out=None), ERR_NULL),
+    (dict(m=129), ERR_SHAPE),             # m % world_size
+    (dict(k=255), ERR_SHAPE),             # k >= 256
+    (dict(k=65535), ERR_SHAPE),           # k < 65535
+    (dict(W=3), ERR_SHAPE),               # world sizes 1, 2, 4, 8, 16, 32
+    (dict(W=64, m=128), ERR_SHAPE),
+    (dict(rank=2), ERR_SHAPE),
+    (dict(nsim=3), ERR_SHAPE),
+    (dict(dt=F32), ERR_DTYPE),
+    (dict(odt=BF16), ERR_DTYPE),          # basic case: output dtype = input dtype
+    (dict(s1=FAKE, s2=FAKE), ERR_DTYPE),  # scales only for int8
+    (dict(dt=I8, odt=BF16), ERR_NULL),    # int8 needs both scales
+    (dict(dt=I8, odt=I32, s1=FAKE), ERR_DTYPE),
+    (dict(dt=I8, odt=F16, s1=FAKE, s2=FAKE, nsim=2), ERR_UNSUP),
+    (dict(dt=I8, odt=I8), ERR_DTYPE),
+    (dict(k=516), ERR_ALIGN),             # k % 8 for 16-bit inputs
+    (dict(n=68), ERR_ALIGN),
+    (dict(dt=I8, odt=I32, n=72), ERR_ALIGN),
+    (dict(x1=FAKE + 8), ERR_ALIGN),
+    (dict(flags=FAKE), ERR_NULL),         # flags need counters
+    (dict(flags=FAKE, cnt=FAKE, epoch=0), ERR_SHAPE),
+])
+def test_mm_rs_rejects(lib, over, code):
+    assert rs(lib, **over) == code
+
+
+def test_ag_mm_rejects(lib):
+    f = lib.mc2_ag_mm_local
+    assert f(None, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_NULL
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 8, 0, BF16, None, FAKE, None, None, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, I8, None, FAKE, None, None, 0, None) == ERR_DTYPE
+    assert f(FAKE, FAKE, 16, 500, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_ALIGN
+    assert f(FAKE, FAKE, 0, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_SHAPE
+
+
+def test_moe_entry_points_reject(lib):
+    assert lib.mc2_moe_histc(FAKE, 10, 0, FAKE, None, None) == ERR_SHAPE
+    assert lib.mc2_moe_histc(FAKE, 10, 1025, FAKE, None, None) == ERR_SHAPE
+    assert lib.mc2_moe_histc(None, 10, 8, FAKE, None, None) == ERR_NULL
+    ws = lib.mc2_moe_permute_workspace_size(32768, 8, 128)
+    assert ws >= 128 * (32768 // 32) * 4
+    P = lib.mc2_moe_permute
+    assert P(FAKE, 100, 64, FAKE, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 0, None, None) == ERR_WS
+    assert P(FAKE, 100, 60, FAKE, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None, None) == ERR_ALIGN
+    assert P(FAKE, 100, 64, FAKE, 65, 16, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, None, None) == ERR_SHAPE
+    assert P(FAKE, 100, 64, FAKE, 8, 16, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None, None) == ERR_NULL
+    D = lib.mc2_gmm_dispatch
+    assert D(FAKE, 100, FAKE, FAKE, 2, 0, 16, 4, FAKE, 64, 64, 1, FAKE, 100, None, None) == ERR_UNSUP
+    assert D(FAKE, 100, FAKE, FAKE, 1, 4, 16, 4, FAKE, 64, 64, 1, FAKE, 100, None, None) == ERR_SHAPE
+    assert D(FAKE, 100, FAKE, FAKE, 1, 0, 16, 5, FAKE, 64, 64, 1, FAKE, 100, None, None) == ERR_SHAPE
+    assert D(FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 72, 1, FAKE, 100, None, None) == ERR_ALIGN
+    assert D(FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 64, 2, FAKE, 100, None, None) == ERR_SHAPE
+    Cb = lib.mc2_gmm_combine
+    assert Cb(FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 60, 64, FAKE, 100, None, None) == ERR_ALIGN
+    assert Cb(None, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 64, FAKE, 100, None, None) == ERR_NULL
+    U = lib.mc2_moe_unpermute
+    assert U(FAKE, 10, FAKE, FAKE, 4, 0, 64, FAKE, None, None) == ERR_SHAPE
+    assert U(FAKE, 10, FAKE, FAKE, 4, 2, 4, FAKE, None, None) == ERR_SHAPE
+    assert U(FAKE, 10, FAKE, FAKE, 4, 2, 68, FAKE, None, None) == ERR_ALIGN

@@ -1,0 +1,192 @@
+"""Parity of the rank-chunked GEMM (MatmulReduceScatter / AllGatherMatmul
+compute share) against the CPU oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gemm_collective_core_amd import mc2
+from gpu_util import DEQUANT_RTOL, assert_rel, assert_tol, to_dev, to_f64, torch_dtype
+from oracle import gemm as og
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_rs(d, W, rank, out_dtype=None, bias=None, flags=None, epoch=0):
+    t = wl.BF16 if d["dtype"] == wl.BF16 else d["dtype"]
+    x1 = to_dev(d["x1"], t)
+    x2 = to_dev(d["x2"], t)
+    kw = {}
+    if "x1_scale" in d and out_dtype != "i32":
+        kw = dict(x1_scale=to_dev(d["x1_scale"]), x2_scale=to_dev(d["x2_scale"]))
+    if bias is not None:
+        kw["bias"] = to_dev(bias, "bf16" if bias.dtype == np.uint16 else None)
+    if flags is not None:
+        kw.update(ready_flags=flags[0], flag_counters=flags[1], epoch=epoch)
+    out = mc2.mc2_mm_rs_local(x1, x2, W, rank, x2_trans=d["x2_trans"],
+                              out_dtype=torch_dtype(out_dtype) if out_dtype else None, **kw)
+    torch.cuda.synchronize()
+    return out
+
+
+def _oracle_rs(d, W, out_dtype=None, bias=None, rows=None, cols=None):
+    kw = {}
+    if "x1_scale" in d and out_dtype != "i32":
+        kw = dict(x1_scale=d["x1_scale"], x2_scale=d["x2_scale"])
+    return og.mm_rs(d["x1"], d["x2"], world_size=W, in_dtype=d["dtype"], nsim=d["nsim"],
+                    x2_trans=d["x2_trans"], bias=bias, out_dtype=out_dtype, rows=rows,
+                    cols=cols, **kw)
+
+
+def test_c1_simulated_w2_reduce_scatter_fp16():
+    """Config 1: two fp16 partials (128,512)x(512,64) summed into two 64-row chunks."""
+    d = wl.c1_inputs()
+    for rank in (0, 1):
+        out = _run_rs(d, 2, rank)
+        ref = _oracle_rs(d, 2)
+        assert_tol(to_f64(out), ref, f"C1 rank {rank}")
+        for c in range(2):
+            rows = og.chunk_rows(128, 2, c)
+            assert_tol(to_f64(out)[rows], ref[rows], f"C1 chunk {c}")
+
+
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+@pytest.mark.parametrize("x2_trans", [False, True])
+@pytest.mark.parametrize("nsim", [1, 4])
+def test_rs_ragged_tiles(dtype, x2_trans, nsim):
+    """Chunks of 200 rows (a ragged 128-row tile), k = 776 (a K tail inside each
+    shard), n = 392 (a ragged column tile); N(0,1) values so the relative term
+    of the gate bites."""
+    W = 4
+    d = wl.gemm_inputs(21, W * 200, 776, 392, dtype, std=1.0, nsim=nsim, x2_trans=x2_trans)
+    out = _run_rs(d, W, 3)
+    assert_tol(to_f64(out), _oracle_rs(d, W), f"rs {dtype} trans={x2_trans} nsim={nsim}")
+    out32 = _run_rs(d, W, 1, out_dtype="f32")
+    ref32 = _oracle_rs(d, W, out_dtype="f32")
+    assert_tol(to_f64(out32), ref32, "fp32 out", rtol=1e-4, atol=1e-3)
+
+
+@pytest.mark.parametrize("nsim", [1, 2])
+def test_rs_bias_added_per_partial(nsim):
+    W = 2
+    d = wl.gemm_inputs(22, 256, 512, 136, wl.BF16, std=1.0, nsim=nsim, bias=True)
+    out = _run_rs(d, W, 0, bias=d["bias"])
+    assert_tol(to_f64(out), _oracle_rs(d, W, bias=d["bias"]), "bias")
+
+
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_int8_raw_accumulator_bit_exact(x2_trans):
+    d = wl.gemm_inputs(23, 4 * 130, 1040, 272, wl.I8, x2_trans=x2_trans)
+    out = _run_rs(d, 4, 0, out_dtype="i32")
+    np.testing.assert_array_equal(to_f64(out), _oracle_rs(d, 4, out_dtype="i32"))
+
+
+def test_int8_extreme_values_bit_exact():
+    """All entries +-127 with k = 65520: |acc| ~ 1.06e9 stays exact in int32."""
+    k, m, n = 65520, 128, 256
+    x1 = np.full((m, k), 127, np.int8)
+    x2 = np.full((k, n), -127, np.int8)
+    x2[:, 1::2] = 127
+    d = {"x1": x1, "x2": x2, "dtype": wl.I8, "nsim": 1, "x2_trans": False}
+    out = _run_rs(d, 1, 0, out_dtype="i32")
+    np.testing.assert_array_equal(to_f64(out), _oracle_rs(d, 1, out_dtype="i32"))
+
+
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_int8_dequant_fp32_and_bf16(x2_trans):
+    d = wl.gemm_inputs(24, 4 * 130, 1040, 272, wl.I8, x2_trans=x2_trans, quant=True)
+    out32 = _run_rs(d, 4, 2, out_dtype="f32")
+    assert_rel(to_f64(out32), _oracle_rs(d, 4, out_dtype="f32"), DEQUANT_RTOL, "dequant fp32")
+    for od in ("bf16", "f16"):
+        out = _run_rs(d, 4, 2, out_dtype=od)
+        assert_tol(to_f64(out), _oracle_rs(d, 4, out_dtype=od), f"dequant {od}")
+
+
+def test_int8_bias_extension():
+    d = wl.gemm_inputs(25, 256, 512, 64, wl.I8, quant=True, bias=True)
+    out = _run_rs(d, 2, 0, out_dtype="f32", bias=d["bias"])
+    ref = og.mm_rs(d["x1"], d["x2"], world_size=2, in_dtype="i8", bias=d["bias"],
+                   bias_dtype="bf16", x1_scale=d["x1_scale"], x2_scale=d["x2_scale"],
+                   out_dtype="f32")
+    assert_rel(to_f64(out), ref, DEQUANT_RTOL, "int8 bias")
+
+
+@pytest.mark.parametrize("rank", [0, 3])
+@pytest.mark.parametrize("x2_trans", [False, True])
+def test_ag_mm_with_flags(rank, x2_trans):
+    W = 8
+    d = wl.gemm_inputs(26, W * 100, 512, 264, wl.BF16, std=1.0, x2_trans=x2_trans)
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
+    x = to_dev(d["x1"], "bf16")
+    w = to_dev(d["x2"], "bf16")
+    for epoch in (7, 8):
+        out = mc2.mc2_ag_mm_local(x, w, W, rank, x2_trans=x2_trans, ready_flags=flags,
+                                  flag_counters=counters, epoch=epoch)
+        torch.cuda.synchronize()
+        assert flags.cpu().tolist() == [epoch] * W
+        assert counters.cpu().tolist() == [0] * W
+    ref = og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16", x2_trans=x2_trans)
+    assert_tol(to_f64(out), ref, "ag_mm")
+
+
+def test_rs_flags_reset_between_calls():
+    W = 4
+    d = wl.gemm_inputs(27, W * 256, 512, 512, wl.BF16, std=1.0)
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
+    for epoch in (1, 2, 3):
+        _run_rs(d, W, 1, flags=(flags, counters), epoch=epoch)
+        assert flags.cpu().tolist() == [epoch] * W
+        assert counters.cpu().tolist() == [0] * W
+
+
+# ------------------------------------------------------------------ full sizes
+
+def _sample(m, W, n, rng, per_chunk=6, ncols=48):
+    rows = np.concatenate([c * (m // W) + rng.choice(m // W, per_chunk, replace=False)
+                           for c in range(W)])
+    cols = np.sort(rng.choice(n, ncols, replace=False))
+    return rows, cols
+
+
+def test_c2_full_ag_mm_sampled():
+    """Config 2 at full size, in the launch configuration the benchmark times."""
+    d = wl.c2_inputs()
+    W = 8
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
+    out = mc2.mc2_ag_mm_local(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 0,
+                              ready_flags=flags, flag_counters=counters, epoch=1)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [1] * W
+    rows, cols = _sample(8192, W, 3072, np.random.default_rng(0))
+    ref = og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16", rows=rows, cols=cols)
+    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, "C2")
+    assert torch.isfinite(out.float()).all()
+
+
+def test_c3_full_int8_sampled():
+    d = wl.c3_inputs()
+    out = _run_rs(d, 4, 0)
+    rows, cols = _sample(4096, 4, 2048, np.random.default_rng(1))
+    ref = _oracle_rs(d, 4, rows=rows, cols=cols)
+    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, "C3 bf16")
+    raw = _run_rs(d, 4, 0, out_dtype="i32")
+    np.testing.assert_array_equal(to_f64(raw)[np.ix_(rows, cols)],
+                                  _oracle_rs(d, 4, out_dtype="i32", rows=rows, cols=cols))
+
+
+def test_c5_full_sampled():
+    a, b = wl.c5_inputs()
+    W = 8
+    out = mc2.mc2_ag_mm_local(to_dev(a["x1"], "bf16"), to_dev(a["x2"], "bf16"), W, 0)
+    torch.cuda.synchronize()
+    rows, cols = _sample(16384, W, 3584, np.random.default_rng(2), per_chunk=4)
+    ref = og.ag_mm(a["x1"], a["x2"], world_size=W, in_dtype="bf16", rows=rows, cols=cols)
+    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, "C5a")
+    del out
+    out = _run_rs(b, W, 0)
+    rows, cols = _sample(16384, W, 8192, np.random.default_rng(3), per_chunk=4)
+    ref = _oracle_rs(b, W, rows=rows, cols=cols)
+    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, "C5b")

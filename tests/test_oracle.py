@@ -400,3 +400,21 @@ def test_router_shapes_ties_and_ranges():
                       local_experts=2, inter=2)
     assert d["sel"].min() >= 0 and d["sel"].max() < 16
     assert all(len(set(r)) == 4 for r in d["sel"].tolist())
+
+
+def test_per_token_outputs_match_the_chain():
+    """Two formulations of the same path agree: per token directly, and
+    through histc -> permute -> grouped fc1/fc2 -> unpermute."""
+    d = wl.moe_inputs(seed=20, tokens=64, hidden=16, num_experts=8, topk=3,
+                      local_experts=4, inter=8)
+    r = moe.moe_local(d["x"], d["sel"], d["probs"], d["w1"], d["w2"], num_experts=8,
+                      ep_rank=1, local_experts=4)
+    toks = np.arange(64)
+    np.testing.assert_array_equal(
+        moe.token_outputs(d["x"], d["sel"], d["probs"], d["w1"], d["w2"], toks, ep_rank=1,
+                          local_experts=4), r["out"])
+    start, n = moe.local_slice(r["counts"], 1, 4)
+    slots = r["permute"]["sorted_idx"][start:start + n]
+    h, y = moe.expert_ffn_rows(d["x"][slots // 3], d["sel"].reshape(-1)[slots] - 4, d["w1"], d["w2"])
+    np.testing.assert_array_equal(h, r["h"])
+    np.testing.assert_array_equal(y, r["y_full"][start:start + n])
