@@ -8,8 +8,10 @@
 // LDS layout of one operand tile: one 128-byte row per output row (A) or per
 // output column (B), K contiguous inside the row, so that every MFMA operand
 // is a single 16-byte LDS read. The eight 16-byte chunks of row r are stored
-// at chunk position (c ^ (r & 7)): eight consecutive rows reading the same
-// logical chunk then hit eight different bank groups.
+// at chunk position c ^ ((r ^ (r >> 3)) & 7): eight consecutive rows reading
+// the same logical chunk hit eight different bank groups (the MFMA operand
+// reads), and so do rows 8 apart writing the same chunk (the transposing
+// store of a row-major B, whose lanes own columns 8 or 16 apart).
 //
 // MFMA shapes: v_mfma_f32_16x16x32_{bf16,f16} and v_mfma_i32_16x16x64_i8. For
 // both, lane l supplies row (l & 15) of A and column (l & 15) of B, and lanes
@@ -24,6 +26,12 @@ namespace mc2 {
 constexpr int kThreads = 256;
 constexpr int kKBytes = 128;
 
+// LDS pointers carry their address space so that every access compiles to a
+// ds_read / ds_write (a generic pointer would become a flat access that waits
+// on the vector memory counter too).
+#define MC2_LDS __attribute__((address_space(3)))
+typedef MC2_LDS char lds_t;
+
 template <int BM_, int BN_, int WM_, int WN_>
 struct TileShape {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -35,25 +43,25 @@ struct TileShape {
 };
 
 __device__ __forceinline__ int lds_off(int r, int c) {
-  return r * kKBytes + ((c ^ (r & 7)) << 4);
+  return r * kKBytes + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
 }
 
 template <Elem E> struct Mma;
 template <> struct Mma<Elem::BF16> {
   using acc_t = f32x4_t;
-  static __device__ __forceinline__ acc_t run(uint4 a, uint4 b, acc_t c) {
+  static __device__ __forceinline__ acc_t run(u32x4_t a, u32x4_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(bit_cast<bf16x8_t>(a), bit_cast<bf16x8_t>(b), c, 0, 0, 0);
   }
 };
 template <> struct Mma<Elem::F16> {
   using acc_t = f32x4_t;
-  static __device__ __forceinline__ acc_t run(uint4 a, uint4 b, acc_t c) {
+  static __device__ __forceinline__ acc_t run(u32x4_t a, u32x4_t b, acc_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(bit_cast<f16x8_t>(a), bit_cast<f16x8_t>(b), c, 0, 0, 0);
   }
 };
 template <> struct Mma<Elem::I8> {
   using acc_t = i32x4_t;
-  static __device__ __forceinline__ acc_t run(uint4 a, uint4 b, acc_t c) {
+  static __device__ __forceinline__ acc_t run(u32x4_t a, u32x4_t b, acc_t c) {
     return __builtin_amdgcn_mfma_i32_16x16x64_i8(bit_cast<i32x4_t>(a), bit_cast<i32x4_t>(b), c, 0, 0, 0);
   }
 };
@@ -68,7 +76,7 @@ struct RowLoader {
   const char* ptr[kPer];
   int chunk;
   int row_base;
-  uint4 v[kPer];
+  u32x4_t v[kPer];
 
   // Rows row0 + r are clamped to row_last: rows past the end read a valid row
   // whose results are never stored.
@@ -89,12 +97,12 @@ struct RowLoader {
     const bool ok = chunk * 16 < kvalid;
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      v[i] = ok ? *reinterpret_cast<const uint4*>(ptr[i] + koff) : zero4();
+      v[i] = ok ? *reinterpret_cast<const u32x4_t*>(ptr[i] + koff) : zero_v4();
   }
-  __device__ __forceinline__ void store(char* lds) const {
+  __device__ __forceinline__ void store(lds_t* lds) const {
 #pragma unroll
     for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<uint4*>(lds + lds_off(row_base + i * kRowStep, chunk)) = v[i];
+      *reinterpret_cast<MC2_LDS u32x4_t*>(lds + lds_off(row_base + i * kRowStep, chunk)) = v[i];
   }
 };
 
@@ -115,7 +123,7 @@ struct ColLoader {
   const char* ptr;
   int64_t ld;
   int nb, kb;
-  uint4 v[R];
+  u32x4_t v[R];
 
   static __device__ __forceinline__ int block_of(int tid) { return tid % NB; }
 
@@ -131,10 +139,10 @@ struct ColLoader {
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const bool ok = kb * R + r < krows;
-      v[r] = ok ? *reinterpret_cast<const uint4*>(ptr + koff + r * ld) : zero4();
+      v[r] = ok ? *reinterpret_cast<const u32x4_t*>(ptr + koff + r * ld) : zero_v4();
     }
   }
-  __device__ __forceinline__ void store(char* lds) const {
+  __device__ __forceinline__ void store(lds_t* lds) const {
     uint32_t d[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -155,32 +163,32 @@ struct ColLoader {
         const int bit = r * ES * 8;
         piece[bit >> 5] |= e << (bit & 31);
       }
-      char* dst = lds + lds_off(nb * CPB + j, ch) + within;
+      lds_t* dst = lds + lds_off(nb * CPB + j, ch) + within;
       if constexpr (PIECE == 16)
-        *reinterpret_cast<uint4*>(dst) = make_uint4(piece[0], piece[1], piece[2], piece[3]);
+        *reinterpret_cast<MC2_LDS u32x4_t*>(dst) = u32x4_t{piece[0], piece[1], piece[2], piece[3]};
       else if constexpr (PIECE == 8)
-        *reinterpret_cast<uint2*>(dst) = make_uint2(piece[0], piece[1]);
+        *reinterpret_cast<MC2_LDS u32x2_t*>(dst) = u32x2_t{piece[0], piece[1]};
       else
-        *reinterpret_cast<uint32_t*>(dst) = piece[0];
+        *reinterpret_cast<MC2_LDS uint32_t*>(dst) = piece[0];
     }
   }
 };
 
 // MFMAs of one 128-byte K tile on the wave's FM x FN fragments.
 template <Elem E, class TS>
-__device__ __forceinline__ void mma_ktile(const char* lA, const char* lB,
+__device__ __forceinline__ void mma_ktile(const lds_t* lA, const lds_t* lB,
                                           typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
                                           int wrow0, int wcol0, int lane) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     const int ch = ks * 4 + (lane >> 4);
-    uint4 a[TS::FM], b[TS::FN];
+    u32x4_t a[TS::FM], b[TS::FN];
 #pragma unroll
     for (int fm = 0; fm < TS::FM; ++fm)
-      a[fm] = *reinterpret_cast<const uint4*>(lA + lds_off(wrow0 + fm * 16 + (lane & 15), ch));
+      a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lA + lds_off(wrow0 + fm * 16 + (lane & 15), ch));
 #pragma unroll
     for (int fn = 0; fn < TS::FN; ++fn)
-      b[fn] = *reinterpret_cast<const uint4*>(lB + lds_off(wcol0 + fn * 16 + (lane & 15), ch));
+      b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lB + lds_off(wcol0 + fn * 16 + (lane & 15), ch));
 #pragma unroll
     for (int fm = 0; fm < TS::FM; ++fm)
 #pragma unroll
@@ -210,7 +218,7 @@ struct BDesc {
 // gives the global column of tile column j (j a multiple of the column block);
 // for B as (n, k) (BT == true) tile column j is global column col0 + j.
 template <Elem E, bool BT, class TS, class ColMap>
-__device__ __forceinline__ void mainloop(char* smem, const char* A, int64_t lda, int64_t row0,
+__device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                          int64_t row_last, const BDesc& B, int64_t col0,
                                          const ColMap& colmap, const KSpan& ks,
                                          typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN]) {
@@ -237,7 +245,7 @@ __device__ __forceinline__ void mainloop(char* smem, const char* A, int64_t lda,
     lb.init(B.base, B.ld, c, tid);
   }
 
-  char* stage[2] = {smem, smem + TS::kStageBytes};
+
   auto issue = [&](int it) {
     const int w = it / ks.ktiles;
     const int kt = it - w * ks.ktiles;
@@ -248,20 +256,21 @@ __device__ __forceinline__ void mainloop(char* smem, const char* A, int64_t lda,
     else
       lb.load(w * ks.b_shard + kdone * B.ld, ks.k - kdone);
   };
-  auto commit = [&](char* s) {
+  auto commit = [&](lds_t* s) {
     la.store(s);
     lb.store(s + TS::BM * kKBytes);
   };
 
   issue(0);
-  commit(stage[0]);
+  commit(smem);
   __syncthreads();
   for (int it = 0; it < ks.niters; ++it) {
-    char* cur = stage[it & 1];
+    lds_t* cur = smem + (it & 1) * TS::kStageBytes;
+    lds_t* nxt = smem + ((it + 1) & 1) * TS::kStageBytes;
     const bool more = it + 1 < ks.niters;
     if (more) issue(it + 1);
     mma_ktile<E, TS>(cur, cur + TS::BM * kKBytes, acc, wrow0, wcol0, lane);
-    if (more) commit(stage[(it + 1) & 1]);
+    if (more) commit(nxt);
     __syncthreads();
   }
 }
@@ -270,7 +279,7 @@ __device__ __forceinline__ void mainloop(char* smem, const char* A, int64_t lda,
 // memory with 16-byte coalesced stores; rows >= nrows and columns >= ncols of
 // the destination are skipped.
 template <int BM>
-__device__ __forceinline__ void store_staged(const char* smem, int pitch, int tile_row_bytes,
+__device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int tile_row_bytes,
                                              char* out, int64_t ldo, int64_t nrows,
                                              int64_t col_byte0, int64_t row_bytes_valid) {
   const int cpr = tile_row_bytes / 16;
@@ -278,8 +287,8 @@ __device__ __forceinline__ void store_staged(const char* smem, int pitch, int ti
   for (int q = threadIdx.x; q < total; q += kThreads) {
     const int r = q / cpr, c = q - r * cpr;
     if (r < nrows && col_byte0 + c * 16 < row_bytes_valid)
-      *reinterpret_cast<uint4*>(out + r * ldo + col_byte0 + c * 16) =
-          *reinterpret_cast<const uint4*>(smem + r * pitch + c * 16);
+      *reinterpret_cast<u32x4_t*>(out + r * ldo + col_byte0 + c * 16) =
+          *reinterpret_cast<const MC2_LDS u32x4_t*>(smem + r * pitch + c * 16);
   }
 }
 

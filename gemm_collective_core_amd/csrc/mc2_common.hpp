@@ -10,6 +10,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -52,6 +54,7 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t b) {
 }
 
 __device__ __forceinline__ uint4 zero4() { return make_uint4(0u, 0u, 0u, 0u); }
+__device__ __forceinline__ u32x4_t zero_v4() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
 __device__ __forceinline__ void atomic_or_err(int32_t* dev_err, uint32_t bit) {
   if (dev_err) atomicOr(dev_err, static_cast<int32_t>(bit));

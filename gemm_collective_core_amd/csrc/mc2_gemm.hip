@@ -8,6 +8,7 @@
 
 #include "../../include/mc2.h"
 #include "gemm_core.hpp"
+#include "gemm8.hpp"
 #include "mc2_host.hpp"
 
 namespace mc2 {
@@ -15,10 +16,10 @@ namespace mc2 {
 // ---------------------------------------------------------------- epilogues
 
 template <Out O>
-__device__ __forceinline__ void put_out(char* p, float v) {
-  if constexpr (O == Out::BF16) *reinterpret_cast<uint16_t*>(p) = f32_to_bf16_bits(v);
-  else if constexpr (O == Out::F16) *reinterpret_cast<uint16_t*>(p) = f32_to_f16_bits(v);
-  else *reinterpret_cast<float*>(p) = v;
+__device__ __forceinline__ void put_out(lds_t* p, float v) {
+  if constexpr (O == Out::BF16) *reinterpret_cast<MC2_LDS uint16_t*>(p) = f32_to_bf16_bits(v);
+  else if constexpr (O == Out::F16) *reinterpret_cast<MC2_LDS uint16_t*>(p) = f32_to_f16_bits(v);
+  else *reinterpret_cast<MC2_LDS float*>(p) = v;
 }
 
 template <Elem E>
@@ -28,15 +29,14 @@ __device__ __forceinline__ float load_bias(const void* bias, int64_t j) {
   else return bf16_bits_to_f32(b);  // BF16 inputs, and the bf16 bias of int8 inputs
 }
 
-// Stage the wave's accumulators (after the elementwise epilogue) into LDS as
-// the output type, row-major with `pitch` bytes per tile row.
-template <Elem E, class TS, Out O>
-__device__ __forceinline__ void stage_linear(char* smem, int pitch,
-                                             const typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
-                                             int64_t row0, int64_t row_last, int64_t col0, int64_t n,
-                                             const void* bias, float bias_mul, const float* s1,
-                                             const float* s2) {
-  constexpr int OS = OutInfo<O>::bytes;
+// Elementwise epilogue of the linear kernels: for every accumulator element
+// of the wave, computes the output value (bias, dequant) and hands it with its
+// tile-local row and column to `sink`.
+template <Elem E, class TS, Out O, class Sink>
+__device__ __forceinline__ void epilogue_linear(const typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
+                                                int64_t row0, int64_t row_last, int64_t col0,
+                                                int64_t n, const void* bias, float bias_mul,
+                                                const float* s1, const float* s2, Sink&& sink) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
@@ -54,29 +54,34 @@ __device__ __forceinline__ void stage_linear(char* smem, int pitch,
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
-        char* dst = smem + lrow * pitch + lcol * OS;
         if constexpr (E == Elem::I8) {
           if constexpr (O == Out::I32) {
-            *reinterpret_cast<int32_t*>(dst) = acc[fm][fn][i];
+            sink(lrow, lcol, acc[fm][fn][i]);
           } else {
             int64_t grow = row0 + lrow;
             grow = grow < row_last ? grow : row_last;
             const float sc = s1[grow] * sc2;
-            put_out<O>(dst, sc * (static_cast<float>(acc[fm][fn][i]) + bv));
+            sink(lrow, lcol, sc * (static_cast<float>(acc[fm][fn][i]) + bv));
           }
         } else {
-          put_out<O>(dst, acc[fm][fn][i] + bias_mul * bv);
+          sink(lrow, lcol, acc[fm][fn][i] + bias_mul * bv);
         }
       }
     }
   }
 }
 
+template <Out O, class V>
+__device__ __forceinline__ void put_out_global(char* p, V v) {
+  if constexpr (O == Out::I32) *reinterpret_cast<int32_t*>(p) = v;
+  else *reinterpret_cast<float*>(p) = v;
+}
+
 // SwiGLU epilogue: tile column blocks alternate gate (even) and up (odd), so
 // the fragments fn = 2p and 2p + 1 of a lane hold gate and up of the same
 // output column. h = silu(g) * u, silu(g) = g / (1 + exp(-g)), stored as bf16.
 template <class TS>
-__device__ __forceinline__ void stage_swiglu(char* smem, int pitch,
+__device__ __forceinline__ void stage_swiglu(lds_t* smem, int pitch,
                                              const f32x4_t (&acc)[TS::FM][TS::FN]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
@@ -92,7 +97,7 @@ __device__ __forceinline__ void stage_swiglu(char* smem, int pitch,
         const float g = acc[fm][2 * p][i];
         const float u = acc[fm][2 * p + 1][i];
         const float h = g / (1.0f + __expf(-g)) * u;
-        *reinterpret_cast<uint16_t*>(smem + lrow * pitch + lcol * 2) = f32_to_bf16_bits(h);
+        *reinterpret_cast<MC2_LDS uint16_t*>(smem + lrow * pitch + lcol * 2) = f32_to_bf16_bits(h);
       }
     }
   }
@@ -129,15 +134,18 @@ struct PlainCols {
 
 template <class TS, int OS>
 constexpr int chunked_smem() {
-  return (2 * TS::kStageBytes) > (TS::BM * (TS::BN * OS + 16)) ? 2 * TS::kStageBytes
-                                                                 : TS::BM * (TS::BN * OS + 16);
+  // 32-bit outputs are not staged through LDS
+  return (OS == 4 || 2 * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
+             ? 2 * TS::kStageBytes
+             : TS::BM * (TS::BN * OS + 16);
 }
 
 template <Elem E, bool BT, class TS, Out O>
 __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
   constexpr int OS = OutInfo<O>::bytes;
   constexpr int kSmem = chunked_smem<TS, OS>();
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
+  lds_t* smem = (lds_t*)smem_raw;
 
   const int b = blockIdx.x;
   const int seq = b / p.tiles_per_chunk;
@@ -155,22 +163,103 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
   PlainCols cm{col0, p.n - CPB};
   mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
 
-  constexpr int pitch = TS::BN * OS + 16;
-  stage_linear<E, TS, O>(smem, pitch, acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul,
-                         p.s1, p.s2);
-  __syncthreads();
-  store_staged<TS::BM>(smem, pitch, TS::BN * OS, p.out + row0 * p.ldo, p.ldo, row_end - row0,
-                       col0 * OS, p.n * OS);
+  if constexpr (OS == 2) {
+    // 16-bit outputs: stage the tile in LDS, then 16-byte coalesced stores.
+    constexpr int pitch = TS::BN * OS + 16;
+    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                              [&](int r, int c, float v) { put_out<O>(smem + r * pitch + c * OS, v); });
+    __syncthreads();
+    store_staged<TS::BM>(smem, pitch, TS::BN * OS, p.out + row0 * p.ldo, p.ldo, row_end - row0,
+                         col0 * OS, p.n * OS);
+  } else {
+    // 32-bit test outputs: stored straight from the accumulator layout.
+    char* base = p.out + row0 * p.ldo + col0 * OS;
+    const int64_t nrows = row_end - row0, ncols = p.n - col0;
+    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                              [&](int r, int c, auto v) {
+                                if (r < nrows && c < ncols) put_out_global<O>(base + r * p.ldo + c * OS, v);
+                              });
+  }
 
   if (p.flags) {
-    // Every thread's stores of this tile become visible before the tile is
-    // counted; the last tile of the chunk publishes the epoch.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // The workgroup barrier makes every wave's stores of this tile visible to
+    // thread 0, whose agent-scope release (one L2 write-back per tile) then
+    // covers them before the tile is counted. Only the last tile of a chunk
+    // acquires the other tiles' releases (an acquire invalidates this XCD's
+    // L2, so it is kept off the other tiles) and then publishes the epoch with
+    // a system-scope release store. Each wave first waits for its own stores
+    // to complete, so the write-back issued after the barrier sees them all.
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const uint32_t prev =
-          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (prev + 1 == static_cast<uint32_t>(p.tiles_per_chunk)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+    }
+  }
+}
+
+// Eight-wave variant for 16-bit inputs (see gemm8.hpp); same schedule,
+// epilogue and ready-flag protocol as chunked_gemm_kernel.
+template <class TS, int OS>
+constexpr int chunked8_smem() {
+  return (OS == 4 || 2 * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
+             ? 2 * TS::kStageBytes
+             : TS::BM * (TS::BN * OS + 16);
+}
+
+template <Elem E, bool BT, class TS, Out O>
+__global__ __launch_bounds__(kThreads8, 1) void chunked_gemm8_kernel(ChunkedArgs p) {
+  constexpr int OS = OutInfo<O>::bytes;
+  constexpr int kSmem = chunked8_smem<TS, OS>();
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
+  lds_t* smem = (lds_t*)smem_raw;
+
+  const int b = blockIdx.x;
+  const int seq = b / p.tiles_per_chunk;
+  const int t = b - seq * p.tiles_per_chunk;
+  int c = p.first_chunk + seq;
+  c = c >= p.world ? c - p.world : c;
+  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
+  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * TS::BM;
+  const int64_t row_end = c * p.mc + p.mc;
+  const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
+
+  f32x4_t acc[TS::FM][TS::FN];
+  BDesc bd{p.B, p.ldb, p.n};
+  PlainCols cm{col0, p.n - 8};
+  mainloop8<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
+
+  if constexpr (OS == 2) {
+    constexpr int pitch = TS::BN * OS + 16;
+    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                              [&](int r, int cc, float v) { put_out<O>(smem + r * pitch + cc * OS, v); });
+    __syncthreads();
+    store_staged8(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo, row_end - row0,
+                  col0 * OS, p.n * OS);
+  } else {
+    char* base = p.out + row0 * p.ldo + col0 * OS;
+    const int64_t nrows = row_end - row0, ncols = p.n - col0;
+    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                              [&](int r, int cc, auto v) {
+                                if (r < nrows && cc < ncols) put_out_global<O>(base + r * p.ldo + cc * OS, v);
+                              });
+  }
+
+  if (p.flags) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      const uint32_t prev =
+          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + 1 == static_cast<uint32_t>(p.tiles_per_chunk)) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
@@ -225,7 +314,8 @@ constexpr int grouped_smem() {
 template <class TS, bool GLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
   constexpr int kSmem = grouped_smem<TS, GLU>();
-  __shared__ __attribute__((aligned(16))) char smem[kSmem];
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
+  lds_t* smem = (lds_t*)smem_raw;
   __shared__ int64_t s_gstart[kMaxLocalExperts + 1];
   __shared__ int64_t s_tstart[kMaxLocalExperts + 1];
   __shared__ int64_t s_base;
@@ -303,8 +393,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
     if constexpr (GLU)
       stage_swiglu<TS>(smem, pitch, acc);
     else
-      stage_linear<Elem::BF16, TS, Out::BF16>(smem, pitch, acc, orow0, 0, ocol0, p.n_out, nullptr,
-                                              0.f, nullptr, nullptr);
+      epilogue_linear<Elem::BF16, TS, Out::BF16>(
+          acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
+          [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
     __syncthreads();
     store_staged<TS::BM>(smem, pitch, OUTC * 2, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
                          ocol0 * 2, p.n_out * 2);
@@ -314,12 +405,31 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
 
 // ---------------------------------------------------------------- host side
 
-using TileMain = TileShape<128, 256, 2, 2>;
+#ifndef MC2_MAIN_BM
+#define MC2_MAIN_BM 128
+#endif
+using TileMain = TileShape<MC2_MAIN_BM, 256, 2, 2>;
+
+#ifndef MC2_T8_BM
+#define MC2_T8_BM 256
+#define MC2_T8_BN 256
+#define MC2_T8_WM 2
+#define MC2_T8_WN 4
+#endif
+using Tile16 = Tile8<MC2_T8_BM, MC2_T8_BN, MC2_T8_WM, MC2_T8_WN>;
+
+template <Elem E> struct TileFor { using type = TileMain; };
+template <> struct TileFor<Elem::F16> { using type = Tile16; };
+template <> struct TileFor<Elem::BF16> { using type = Tile16; };
 
 template <Elem E, bool BT, Out O>
 static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TileMain, O>), dim3(blocks), dim3(kThreads), 0, s,
-                     a);
+  if constexpr (E == Elem::I8)
+    hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TileMain, O>), dim3(blocks), dim3(kThreads), 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((chunked_gemm8_kernel<E, BT, Tile16, O>), dim3(blocks), dim3(kThreads8), 0,
+                       s, a);
   return hipGetLastError();
 }
 
@@ -375,8 +485,10 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.mc = m / W;
   a.world = W;
   a.first_chunk = first_chunk;
-  a.tiles_m = static_cast<int>((a.mc + TileMain::BM - 1) / TileMain::BM);
-  a.tiles_n = static_cast<int>((n + TileMain::BN - 1) / TileMain::BN);
+  const int BM = in_dtype == MC2_I8 ? TileMain::BM : Tile16::BM;
+  const int BN = in_dtype == MC2_I8 ? TileMain::BN : Tile16::BN;
+  a.tiles_m = static_cast<int>((a.mc + BM - 1) / BM);
+  a.tiles_n = static_cast<int>((n + BN - 1) / BN);
   a.tiles_per_chunk = a.tiles_m * a.tiles_n;
   a.bias_mul = static_cast<float>(nsim);
   a.flags = flags;
