@@ -6,15 +6,19 @@
 // bounds a GEMM tile on this chip: one CU sustains roughly twice the L2/MALL
 // read bandwidth with eight waves as with four.
 //
-// K advances in stages of 64 elements (128 bytes per row), double-buffered in
-// LDS: the global loads of stage i+1 go to registers while the MFMAs of stage
-// i run, then land in the other LDS buffer.
+// K advances in stages of 32 elements (64 bytes per row) held in a ring of 4
+// LDS buffers. Loads go straight from global memory to LDS (buffer loads with
+// the LDS bit: no registers, and lanes past a buffer's range write zeros,
+// which pads the K tail); three stages are in flight while one is consumed.
+// Each wave waits only for its own loads of the stage it is about to read
+// (vmcnt), then one workgroup barrier per stage both publishes the stage and
+// frees the buffer that the next load overwrites.
 //
 // LDS layouts:
-//  * A (m, k) and B given as (n, k): one 128-byte row per output row/column,
-//    16-byte chunk c of row r stored at c ^ ((r ^ (r >> 3)) & 7) -- the MFMA
+//  * A (m, k) and B given as (n, k): one 64-byte row per output row/column,
+//    16-byte chunk c of row r stored at c ^ ((r >> 2) & 3) -- the MFMA
 //    operand is one 16-byte read, conflict-free for 16 consecutive rows.
-//  * B given row-major as (k, n): kept k-major as loaded (64 rows of BN*2
+//  * B given row-major as (k, n): kept k-major as loaded (32 rows of BN*2
 //    bytes); 32-byte pair q of row k stored at q ^ s(k), s(k) = (k & 3) |
 //    (((k >> 3) & 1) << 2) (k & 3 for rows of fewer than 8 pairs), which keeps
 //    the 16-lane groups of a transposing read on distinct banks. The operand
@@ -37,11 +41,15 @@ struct Tile8 {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "tile not divisible");
-  static_assert(BN % 64 == 0, "B rows are whole 128-byte lines");
-  static constexpr int kABytes = BM * kKBytes;
-  static constexpr int kBBytes = BN * kKBytes;  // same size in both B layouts
+  static_assert(BN % 128 == 0 && BM % 128 == 0, "tile sizes");
+  static constexpr int kRow = 64;                 // bytes of K per row per stage
+  static constexpr int kABytes = BM * kRow;
+  static constexpr int kBBytes = BN * kRow;       // same size in both B layouts
   static constexpr int kStageBytes = kABytes + kBBytes;
+  static constexpr int kStages = 4;
 };
+
+__device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
 
 // K-major B layout (row-major (k, n) input): pair swizzle of k row kr. Rows
 // of at least 8 pairs (BN % 128 == 0) use 3 bits, narrower rows 2 bits.
@@ -56,135 +64,102 @@ __device__ __forceinline__ int kmaj_off(int kr, int ch) {
   return kr * (BN * 2) + ((((ch >> 1) ^ kmaj_swz<BN>(kr)) << 1) | (ch & 1)) * 16;
 }
 
-// Rows of 128 bytes, K-contiguous (A, or B given as (n, k)); 512 threads.
-template <int ROWS>
-struct RowLoader8 {
-  static constexpr int kPer = ROWS * 8 / kThreads8;
-  static constexpr int kRowStep = kThreads8 / 8;
-  static_assert(kPer >= 1 && kPer * kThreads8 == ROWS * 8, "rows per tile");
-  const char* ptr[kPer];
-  int chunk, row_base;
-  u32x4_t v[kPer];
-
-  __device__ __forceinline__ void init(const char* base, int64_t ld, int64_t row0,
-                                       int64_t row_last, int tid) {
-    chunk = tid & 7;
-    row_base = tid >> 3;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      int64_t r = row0 + row_base + i * kRowStep;
-      r = r < row_last ? r : row_last;
-      ptr[i] = base + r * ld + chunk * 16;
-    }
-  }
-  __device__ __forceinline__ void load(int64_t koff, int64_t kvalid) {
-    const bool ok = chunk * 16 < kvalid;
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      v[i] = ok ? *reinterpret_cast<const u32x4_t*>(ptr[i] + koff) : zero_v4();
-  }
-  __device__ __forceinline__ void store(lds_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<MC2_LDS u32x4_t*>(lds + lds_off(row_base + i * kRowStep, chunk)) = v[i];
-  }
-};
-
-// Row-major (k, n) B of 16-bit elements, stored k-major: 64 k rows of BN
-// columns per stage; thread loads 16-byte chunks along n.
-template <int BN>
-struct KMajLoader8 {
-  static constexpr int CPR = BN / 8;                  // chunks per k row
-  static constexpr int kPer = 64 * CPR / kThreads8;   // chunks per thread
-  static constexpr int kRowStep = kThreads8 / CPR;    // k rows per pass
-  static_assert(kPer >= 1 && kPer * kThreads8 == 64 * CPR, "B tile split");
-  const char* ptr;
-  int64_t ld;
-  int ch, kr0;
-  u32x4_t v[kPer];
-
-  // col_elem: global column of this thread's chunk (already clamped).
-  static __device__ __forceinline__ int chunk_of(int tid) { return tid % CPR; }
-  __device__ __forceinline__ void init(const char* base, int64_t ldb, int64_t col_elem, int tid) {
-    ch = tid % CPR;
-    kr0 = tid / CPR;
-    ld = ldb;
-    ptr = base + col_elem * 2 + static_cast<int64_t>(kr0) * ldb;
-  }
-  // koff: byte offset of the first k row of the stage; krows: k rows left.
-  __device__ __forceinline__ void load(int64_t koff, int64_t krows) {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const bool ok = kr0 + i * kRowStep < krows;
-      v[i] = ok ? *reinterpret_cast<const u32x4_t*>(ptr + koff + (int64_t)(i * kRowStep) * ld)
-                : zero_v4();
-    }
-  }
-  __device__ __forceinline__ void store(lds_t* lds) const {
-#pragma unroll
-    for (int i = 0; i < kPer; ++i)
-      *reinterpret_cast<MC2_LDS u32x4_t*>(lds + kmaj_off<BN>(kr0 + i * kRowStep, ch)) = v[i];
-  }
-};
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
 // B operand of one 16-column block from the k-major layout: two transposing
 // 64-bit reads (k values 8g..8g+3 and 8g+4..8g+7 of column n0 + (lane & 15)).
+// The reads are issued as inline assembly: the compiler cannot tell that they
+// do not overlap the LDS stages still being filled by in-flight loads and
+// would otherwise wait for all of them. Their results are consumed only after
+// lds_wait_tied() below.
 template <int BN>
-__device__ __forceinline__ u32x4_t read_b_kmaj(const lds_t* lB, int ks, int n0, int lane) {
+__device__ __forceinline__ u32x4_t read_b_kmaj(const lds_t* lB, int n0, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int q = n0 >> 4;
   u32x4_t out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int kr = ks * 32 + g * 8 + h * 4 + (j >> 2);
+    const int kr = g * 8 + h * 4 + (j >> 2);
     const int off = kr * (BN * 2) + ((q ^ kmaj_swz<BN>(kr)) << 5) + ((j & 3) << 3);
-    const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (MC2_LDS v4i16_t*)(const_cast<lds_t*>(lB) + off));
-    const u32x2_t w = bit_cast<u32x2_t>(r);
+    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lB + off));
+    u32x2_t w;
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
     out[2 * h] = w[0];
     out[2 * h + 1] = w[1];
   }
   return out;
 }
 
-// MFMAs of one 128-byte K stage on the wave's FM x FN fragments.
+// Waits for all outstanding LDS reads; the fragments are tied to the wait so
+// that no instruction using them is scheduled before it.
+template <int N>
+__device__ __forceinline__ void lds_wait_tied(u32x4_t (&v)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+}
+
+// MFMAs of one K stage (32 values) on the wave's FM x FN fragments.
 template <Elem E, class TS, bool BT>
 __device__ __forceinline__ void mma_stage8(const lds_t* lA, const lds_t* lB,
                                            f32x4_t (&acc)[TS::FM][TS::FN], int wrow0, int wcol0,
                                            int lane) {
+  const int ch = lane >> 4;
+  u32x4_t a[TS::FM], b[TS::FN];
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int ch = ks * 4 + (lane >> 4);
-    u32x4_t a[TS::FM], b[TS::FN];
-#pragma unroll
-    for (int fn = 0; fn < TS::FN; ++fn) {
-      if constexpr (BT)
-        b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lB + lds_off(wcol0 + fn * 16 + (lane & 15), ch));
-      else
-        b[fn] = read_b_kmaj<TS::BN>(lB, ks, wcol0 + fn * 16, lane);
-    }
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm)
-      a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lA + lds_off(wrow0 + fm * 16 + (lane & 15), ch));
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < TS::FN; ++fn)
-        acc[fm][fn] = Mma<E>::run(a[fm], b[fn], acc[fm][fn]);
+  for (int fn = 0; fn < TS::FN; ++fn) {
+    if constexpr (BT)
+      b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lB + lds_off64(wcol0 + fn * 16 + (lane & 15), ch));
+    else
+      b[fn] = read_b_kmaj<TS::BN>(lB, wcol0 + fn * 16, lane);
   }
+#pragma unroll
+  for (int fm = 0; fm < TS::FM; ++fm)
+    a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lA + lds_off64(wrow0 + fm * 16 + (lane & 15), ch));
+  if constexpr (!BT) lds_wait_tied(b);
+#pragma unroll
+  for (int fm = 0; fm < TS::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < TS::FN; ++fn)
+      acc[fm][fn] = Mma<E>::run(a[fm], b[fn], acc[fm][fn]);
+}
+
+constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
+constexpr uint32_t kOffNone = 0x80000000u;   // an offset past every range: loads zero
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, 0x7ffffff0, kBufFlags);
+}
+
+// One 16-byte-per-lane load from `rsrc` at `voff` into LDS at `lds` (wave
+// uniform) + 16 * lane.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_t* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (MC2_LDS void*)lds, 16, voff, 0, 0, 0);
+}
+
+// Workgroup barrier that neither waits on outstanding loads nor lets the
+// compiler move memory accesses across it.
+__device__ __forceinline__ void bar_sync() {
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
 // Main loop over all K stages of all shards (see KSpan). For row-major B,
 // `colmap(c)` gives the global column of tile column c (c a multiple of 8).
+// Each wave issues two 1 KiB loads for A and two for B per stage.
 template <Elem E, bool BT, class TS, class ColMap>
 __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                           int64_t row_last, const BDesc& B, int64_t col0,
                                           const ColMap& colmap, const KSpan& ks,
                                           f32x4_t (&acc)[TS::FM][TS::FN]) {
   static_assert(ElemInfo<E>::bytes == 2, "16-bit inputs");
-  constexpr int KE = 64;
+  static_assert(TS::BM / 16 == 16 && TS::BN / 16 == 16, "two A and two B loads per wave");
+  constexpr int KE = 32;
+  constexpr int S = TS::kStages;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
@@ -194,42 +169,82 @@ __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t ld
 #pragma unroll
     for (int fn = 0; fn < TS::FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  RowLoader8<TS::BM> la;
-  la.init(A, lda, row0, row_last, tid);
-  using BL = typename std::conditional<BT, RowLoader8<TS::BN>, KMajLoader8<TS::BN>>::type;
-  BL lb;
-  if constexpr (BT)
-    lb.init(B.base, B.ld, col0, B.n - 1, tid);
-  else
-    lb.init(B.base, B.ld, colmap(BL::chunk_of(tid) * 8), tid);
+  // Per-lane offsets of this wave's loads (rows fixed; K moves the base).
+  // A: load j covers tile rows 16*(2*wave + j) .. +15; lane -> row + lane/4,
+  // physical chunk lane & 3 holding logical chunk (lane & 3) ^ ((row >> 2) & 3).
+  uint32_t a_off[2], b_off[2];
+  int a_chunk[2], b_key[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 16 * (2 * wave + j) + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    int64_t gr = row0 + r;
+    gr = gr < row_last ? gr : row_last;
+    a_off[j] = static_cast<uint32_t>((gr - row0) * lda + c * 16);
+    a_chunk[j] = c;
+    if constexpr (BT) {
+      int64_t gc = col0 + r;
+      gc = gc < B.n - 1 ? gc : B.n - 1;
+      b_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
+      b_key[j] = c;
+    } else {
+      // k-major: load j covers k rows 2*(2*wave + j) .. +1, lane -> k row
+      // + lane/32, physical chunk lane & 31.
+      const int kr = 2 * (2 * wave + j) + (lane >> 5);
+      const int pc = lane & 31;
+      const int ch = ((((pc >> 1) ^ kmaj_swz<TS::BN>(kr))) << 1) | (pc & 1);
+      const int64_t gcol = colmap(ch * 8);
+      b_off[j] = static_cast<uint32_t>(kr * B.ld + gcol * 2);
+      b_key[j] = kr;
+    }
+  }
+  const char* a_base = A + row0 * lda;
+  const char* b_base = BT ? B.base + col0 * B.ld : B.base;
 
   auto issue = [&](int it) {
     const int w = it / ks.ktiles;
     const int kt = it - w * ks.ktiles;
     const int64_t kdone = static_cast<int64_t>(kt) * KE;
-    la.load(w * ks.a_shard + kdone * 2, (ks.k - kdone) * 2);
-    if constexpr (BT)
-      lb.load(w * ks.b_shard + kdone * 2, (ks.k - kdone) * 2);
-    else
-      lb.load(w * ks.b_shard + kdone * B.ld, ks.k - kdone);
-  };
-  auto commit = [&](lds_t* s) {
-    la.store(s);
-    lb.store(s + TS::kABytes);
+    lds_t* st = smem + (it % S) * TS::kStageBytes;
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + w * ks.a_shard + kdone * 2);
+    const int64_t kleft = ks.k - kdone;  // K values left in this shard
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool ok = a_chunk[j] * 8 < kleft;
+      dma16(ra, st + 16 * (2 * wave + j) * 64, ok ? a_off[j] : kOffNone);
+    }
+    if constexpr (BT) {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * 2);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = b_key[j] * 8 < kleft;
+        dma16(rb, st + TS::kABytes + 16 * (2 * wave + j) * 64, ok ? b_off[j] : kOffNone);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * B.ld);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const bool ok = b_key[j] < kleft;
+        dma16(rb, st + TS::kABytes + 2 * (2 * wave + j) * (TS::BN * 2), ok ? b_off[j] : kOffNone);
+      }
+    }
   };
 
-  issue(0);
-  commit(smem);
-  __syncthreads();
-  for (int it = 0; it < ks.niters; ++it) {
-    lds_t* cur = smem + (it & 1) * TS::kStageBytes;
-    lds_t* nxt = smem + ((it + 1) & 1) * TS::kStageBytes;
-    const bool more = it + 1 < ks.niters;
-    if (more) issue(it + 1);
+  const int n = ks.niters;
+#pragma unroll
+  for (int p = 0; p < S - 1; ++p)
+    if (p < n) issue(p);
+  for (int it = 0; it < n; ++it) {
+    // Own loads of stage `it` done: the stages issued after it may stay in flight.
+    if (it + 2 < n) wait_vmcnt<8>();
+    else if (it + 1 < n) wait_vmcnt<4>();
+    else wait_vmcnt<0>();
+    bar_sync();
+    if (it + S - 1 < n) issue(it + S - 1);
+    const lds_t* cur = smem + (it % S) * TS::kStageBytes;
     mma_stage8<E, TS, BT>(cur, cur + TS::kABytes, acc, wrow0, wcol0, lane);
-    if (more) commit(nxt);
-    __syncthreads();
   }
+  bar_sync();
 }
 
 // Staged tile -> global with 16-byte coalesced stores, 512 threads.

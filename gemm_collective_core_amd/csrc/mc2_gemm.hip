@@ -208,8 +208,8 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
 // epilogue and ready-flag protocol as chunked_gemm_kernel.
 template <class TS, int OS>
 constexpr int chunked8_smem() {
-  return (OS == 4 || 2 * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
-             ? 2 * TS::kStageBytes
+  return (OS == 4 || TS::kStages * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
+             ? TS::kStages * TS::kStageBytes
              : TS::BM * (TS::BN * OS + 16);
 }
 
@@ -476,7 +476,9 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.lda = k * es;
   a.ldb = (x2_trans ? k : n) * es;
   a.ldo = n * os;
-  const int ke = kKBytes / es;
+  // K values per main-loop stage: 32 in the eight-wave 16-bit loop, 128 bytes
+  // of int8 in the four-wave loop.
+  const int ke = in_dtype == MC2_I8 ? kKBytes : Tile16::kRow / 2;
   a.ks.k = k;
   a.ks.a_shard = m * k * es;
   a.ks.b_shard = k * n * es;
