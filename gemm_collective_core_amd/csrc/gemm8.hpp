@@ -34,7 +34,7 @@ namespace mc2 {
 
 constexpr int kThreads8 = 512;
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int KR_ = 128, int S_ = 2>
 struct Tile8 {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static_assert(WM * WN == 8, "eight waves per workgroup");
@@ -42,14 +42,25 @@ struct Tile8 {
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "tile not divisible");
   static_assert(BN % 128 == 0 && BM % 128 == 0, "tile sizes");
-  static constexpr int kRow = 64;                 // bytes of K per row per stage
+  static constexpr int kRow = KR_;                // bytes of K per row per stage (64 or 128)
+  static constexpr int kKE = KR_ / 2;             // K values per stage
+  static constexpr int kSteps = kKE / 32;         // MFMA k-steps per stage
   static constexpr int kABytes = BM * kRow;
   static constexpr int kBBytes = BN * kRow;       // same size in both B layouts
   static constexpr int kStageBytes = kABytes + kBBytes;
-  static constexpr int kStages = 4;
+  static constexpr int kStages = S_;
+  static_assert(KR_ == 64 || KR_ == 128, "stage depth");
 };
 
-__device__ __forceinline__ int lds_off64(int r, int c) { return r * 64 + ((c ^ ((r >> 2) & 3)) << 4); }
+// Byte offset of 16-byte chunk c of row r in a K-contiguous stage with rows of
+// KR bytes: 128-byte rows swizzle c ^ ((r ^ (r >> 3)) & 7), 64-byte rows
+// c ^ ((r >> 2) & 3); both keep 16 consecutive rows reading the same logical
+// chunk on distinct banks.
+template <int KR>
+__device__ __forceinline__ int row_off(int r, int c) {
+  if constexpr (KR == 128) return r * 128 + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+  else return r * 64 + ((c ^ ((r >> 2) & 3)) << 4);
+}
 
 // K-major B layout (row-major (k, n) input): pair swizzle of k row kr. Rows
 // of at least 8 pairs (BN % 128 == 0) use 3 bits, narrower rows 2 bits.
@@ -71,13 +82,13 @@ __device__ __forceinline__ int kmaj_off(int kr, int ch) {
 // would otherwise wait for all of them. Their results are consumed only after
 // lds_wait_tied() below.
 template <int BN>
-__device__ __forceinline__ u32x4_t read_b_kmaj(const lds_t* lB, int n0, int lane) {
+__device__ __forceinline__ u32x4_t read_b_kmaj(const lds_t* lB, int ks, int n0, int lane) {
   const int g = lane >> 4, j = lane & 15;
   const int q = n0 >> 4;
   u32x4_t out;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const int kr = g * 8 + h * 4 + (j >> 2);
+    const int kr = ks * 32 + g * 8 + h * 4 + (j >> 2);
     const int off = kr * (BN * 2) + ((q ^ kmaj_swz<BN>(kr)) << 5) + ((j & 3) << 3);
     const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lB + off));
     u32x2_t w;
@@ -97,29 +108,34 @@ __device__ __forceinline__ void lds_wait_tied(u32x4_t (&v)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
 }
 
-// MFMAs of one K stage (32 values) on the wave's FM x FN fragments.
+// MFMAs of one K stage on the wave's FM x FN fragments.
 template <Elem E, class TS, bool BT>
 __device__ __forceinline__ void mma_stage8(const lds_t* lA, const lds_t* lB,
                                            f32x4_t (&acc)[TS::FM][TS::FN], int wrow0, int wcol0,
                                            int lane) {
-  const int ch = lane >> 4;
-  u32x4_t a[TS::FM], b[TS::FN];
 #pragma unroll
-  for (int fn = 0; fn < TS::FN; ++fn) {
-    if constexpr (BT)
-      b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lB + lds_off64(wcol0 + fn * 16 + (lane & 15), ch));
-    else
-      b[fn] = read_b_kmaj<TS::BN>(lB, wcol0 + fn * 16, lane);
+  for (int ks = 0; ks < TS::kSteps; ++ks) {
+    const int ch = ks * 4 + (lane >> 4);
+    u32x4_t a[TS::FM], b[TS::FN];
+#pragma unroll
+    for (int fn = 0; fn < TS::FN; ++fn) {
+      if constexpr (BT)
+        b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(
+            lB + row_off<TS::kRow>(wcol0 + fn * 16 + (lane & 15), ch));
+      else
+        b[fn] = read_b_kmaj<TS::BN>(lB, ks, wcol0 + fn * 16, lane);
+    }
+#pragma unroll
+    for (int fm = 0; fm < TS::FM; ++fm)
+      a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(
+          lA + row_off<TS::kRow>(wrow0 + fm * 16 + (lane & 15), ch));
+    if constexpr (!BT) lds_wait_tied(b);
+#pragma unroll
+    for (int fm = 0; fm < TS::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < TS::FN; ++fn)
+        acc[fm][fn] = Mma<E>::run(a[fm], b[fn], acc[fm][fn]);
   }
-#pragma unroll
-  for (int fm = 0; fm < TS::FM; ++fm)
-    a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lA + lds_off64(wrow0 + fm * 16 + (lane & 15), ch));
-  if constexpr (!BT) lds_wait_tied(b);
-#pragma unroll
-  for (int fm = 0; fm < TS::FM; ++fm)
-#pragma unroll
-    for (int fn = 0; fn < TS::FN; ++fn)
-      acc[fm][fn] = Mma<E>::run(a[fm], b[fn], acc[fm][fn]);
 }
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
@@ -143,23 +159,33 @@ __device__ __forceinline__ void bar_sync() {
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N == 0 || N == 4 || N == 8 || N == 16, "vmcnt");
   if constexpr (N == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   else if constexpr (N == 4) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if constexpr (N == 8) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
 }
 
 // Main loop over all K stages of all shards (see KSpan). For row-major B,
 // `colmap(c)` gives the global column of tile column c (c a multiple of 8).
-// Each wave issues two 1 KiB loads for A and two for B per stage.
+// Every load instruction moves 1 KiB (64 lanes x 16 bytes): RPI rows of kRow
+// bytes for A and for B given as (n, k), two k rows of BN columns for
+// row-major B; each wave issues NA + NB of them per stage.
 template <Elem E, bool BT, class TS, class ColMap>
 __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                           int64_t row_last, const BDesc& B, int64_t col0,
                                           const ColMap& colmap, const KSpan& ks,
                                           f32x4_t (&acc)[TS::FM][TS::FN]) {
   static_assert(ElemInfo<E>::bytes == 2, "16-bit inputs");
-  static_assert(TS::BM / 16 == 16 && TS::BN / 16 == 16, "two A and two B loads per wave");
-  constexpr int KE = 32;
-  constexpr int S = TS::kStages;
+  constexpr int KR = TS::kRow, KE = TS::kKE, S = TS::kStages;
+  constexpr int RPI = 1024 / KR;                 // rows per load instruction
+  constexpr int LPR = KR / 16;                   // lanes per row
+  constexpr int NA = TS::BM / RPI / 8;           // A loads per wave per stage
+  constexpr int NBT = TS::BN / RPI / 8;          // B (n, k) loads per wave per stage
+  constexpr int NBN = KE / 2 / 8;                // B (k, n) loads per wave per stage
+  static_assert(TS::BN == 256, "row-major B loads cover two k rows of 256 columns");
+  constexpr int NB = BT ? NBT : NBN;
+  constexpr int D = NA + NB;                     // loads per wave per stage
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
@@ -170,27 +196,30 @@ __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t ld
     for (int fn = 0; fn < TS::FN; ++fn) acc[fm][fn] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Per-lane offsets of this wave's loads (rows fixed; K moves the base).
-  // A: load j covers tile rows 16*(2*wave + j) .. +15; lane -> row + lane/4,
-  // physical chunk lane & 3 holding logical chunk (lane & 3) ^ ((row >> 2) & 3).
-  uint32_t a_off[2], b_off[2];
-  int a_chunk[2], b_key[2];
+  uint32_t a_off[NA], b_off[NB];
+  int a_key[NA], b_key[NB];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = 16 * (2 * wave + j) + (lane >> 2);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+  for (int j = 0; j < NA; ++j) {
+    const int r = RPI * (NA * wave + j) + lane / LPR;
+    const int pc = lane % LPR;
+    const int c = (row_off<KR>(r, pc) - r * KR) >> 4;  // swizzle is an involution
     int64_t gr = row0 + r;
     gr = gr < row_last ? gr : row_last;
     a_off[j] = static_cast<uint32_t>((gr - row0) * lda + c * 16);
-    a_chunk[j] = c;
+    a_key[j] = c;
+  }
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
     if constexpr (BT) {
+      const int r = RPI * (NB * wave + j) + lane / LPR;
+      const int pc = lane % LPR;
+      const int c = (row_off<KR>(r, pc) - r * KR) >> 4;
       int64_t gc = col0 + r;
       gc = gc < B.n - 1 ? gc : B.n - 1;
       b_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
       b_key[j] = c;
     } else {
-      // k-major: load j covers k rows 2*(2*wave + j) .. +1, lane -> k row
-      // + lane/32, physical chunk lane & 31.
-      const int kr = 2 * (2 * wave + j) + (lane >> 5);
+      const int kr = 2 * (NB * wave + j) + (lane >> 5);
       const int pc = lane & 31;
       const int ch = ((((pc >> 1) ^ kmaj_swz<TS::BN>(kr))) << 1) | (pc & 1);
       const int64_t gcol = colmap(ch * 8);
@@ -206,27 +235,23 @@ __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t ld
     const int kt = it - w * ks.ktiles;
     const int64_t kdone = static_cast<int64_t>(kt) * KE;
     lds_t* st = smem + (it % S) * TS::kStageBytes;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + w * ks.a_shard + kdone * 2);
     const int64_t kleft = ks.k - kdone;  // K values left in this shard
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + w * ks.a_shard + kdone * 2);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bool ok = a_chunk[j] * 8 < kleft;
-      dma16(ra, st + 16 * (2 * wave + j) * 64, ok ? a_off[j] : kOffNone);
-    }
+    for (int j = 0; j < NA; ++j)
+      dma16(ra, st + RPI * (NA * wave + j) * KR, a_key[j] * 8 < kleft ? a_off[j] : kOffNone);
     if constexpr (BT) {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * 2);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool ok = b_key[j] * 8 < kleft;
-        dma16(rb, st + TS::kABytes + 16 * (2 * wave + j) * 64, ok ? b_off[j] : kOffNone);
-      }
+      for (int j = 0; j < NB; ++j)
+        dma16(rb, st + TS::kABytes + RPI * (NB * wave + j) * KR,
+              b_key[j] * 8 < kleft ? b_off[j] : kOffNone);
     } else {
       const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * B.ld);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bool ok = b_key[j] < kleft;
-        dma16(rb, st + TS::kABytes + 2 * (2 * wave + j) * (TS::BN * 2), ok ? b_off[j] : kOffNone);
-      }
+      for (int j = 0; j < NB; ++j)
+        dma16(rb, st + TS::kABytes + 2 * (NB * wave + j) * (TS::BN * 2),
+              b_key[j] < kleft ? b_off[j] : kOffNone);
     }
   };
 
@@ -235,10 +260,17 @@ __device__ __forceinline__ void mainloop8(lds_t* smem, const char* A, int64_t ld
   for (int p = 0; p < S - 1; ++p)
     if (p < n) issue(p);
   for (int it = 0; it < n; ++it) {
-    // Own loads of stage `it` done: the stages issued after it may stay in flight.
-    if (it + 2 < n) wait_vmcnt<8>();
-    else if (it + 1 < n) wait_vmcnt<4>();
-    else wait_vmcnt<0>();
+    // Own loads of stage `it` done; the stages issued after it may stay in flight.
+    if constexpr (S == 4) {
+      if (it + 2 < n) wait_vmcnt<2 * D>();
+      else if (it + 1 < n) wait_vmcnt<D>();
+      else wait_vmcnt<0>();
+    } else if constexpr (S == 3) {
+      if (it + 1 < n) wait_vmcnt<D>();
+      else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
+    }
     bar_sync();
     if (it + S - 1 < n) issue(it + S - 1);
     const lds_t* cur = smem + (it % S) * TS::kStageBytes;

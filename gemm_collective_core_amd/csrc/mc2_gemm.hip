@@ -410,13 +410,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
 #endif
 using TileMain = TileShape<MC2_MAIN_BM, 256, 2, 2>;
 
-#ifndef MC2_T8_BM
-#define MC2_T8_BM 256
-#define MC2_T8_BN 256
-#define MC2_T8_WM 2
-#define MC2_T8_WN 4
+#ifndef MC2_T8_KR
+#define MC2_T8_KR 128
+#define MC2_T8_S 2
 #endif
-using Tile16 = Tile8<MC2_T8_BM, MC2_T8_BN, MC2_T8_WM, MC2_T8_WN>;
+using Tile16 = Tile8<256, 256, 2, 4, MC2_T8_KR, MC2_T8_S>;
 
 template <Elem E> struct TileFor { using type = TileMain; };
 template <> struct TileFor<Elem::F16> { using type = Tile16; };
@@ -478,7 +476,7 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.ldo = n * os;
   // K values per main-loop stage: 32 in the eight-wave 16-bit loop, 128 bytes
   // of int8 in the four-wave loop.
-  const int ke = in_dtype == MC2_I8 ? kKBytes : Tile16::kRow / 2;
+  const int ke = in_dtype == MC2_I8 ? kKBytes : Tile16::kKE;
   a.ks.k = k;
   a.ks.a_shard = m * k * es;
   a.ks.b_shard = k * n * es;
