@@ -4,11 +4,8 @@
 // Formulas: torch_npu.npu_mm_reduce_scatter_base API doc, "功能说明" (basic and
 // quantized MatmulReduceScatter); CANN hccl issue 158 (AllGatherMatmul);
 // "NPU Training Operators - MC2", "执行路径" (GroupedMatmul fc1 + swiglu, fc2).
-#include <type_traits>
-
 #include "../../include/mc2.h"
 #include "gemm_core.hpp"
-#include "gemm8.hpp"
 #include "mc2_host.hpp"
 
 namespace mc2 {
@@ -22,6 +19,12 @@ __device__ __forceinline__ void put_out(lds_t* p, float v) {
   else *reinterpret_cast<MC2_LDS float*>(p) = v;
 }
 
+template <Out O, class V>
+__device__ __forceinline__ void put_out_global(char* p, V v) {
+  if constexpr (O == Out::I32) *reinterpret_cast<int32_t*>(p) = v;
+  else *reinterpret_cast<float*>(p) = v;
+}
+
 template <Elem E>
 __device__ __forceinline__ float load_bias(const void* bias, int64_t j) {
   const uint16_t b = static_cast<const uint16_t*>(bias)[j];
@@ -30,8 +33,11 @@ __device__ __forceinline__ float load_bias(const void* bias, int64_t j) {
 }
 
 // Elementwise epilogue of the linear kernels: for every accumulator element
-// of the wave, computes the output value (bias, dequant) and hands it with its
-// tile-local row and column to `sink`.
+// of the wave, computes the output value and hands it with its tile-local row
+// and column to `sink`.
+//   16-bit inputs: acc + bias_mul * bias[j]  (bias_mul = number of partials)
+//   int8 inputs:   (x1_scale[i] * x2_scale[j]) * (float(acc) + bias[j]),
+//                  or the raw accumulator for 32-bit integer output
 template <Elem E, class TS, Out O, class Sink>
 __device__ __forceinline__ void epilogue_linear(const typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
                                                 int64_t row0, int64_t row_last, int64_t col0,
@@ -69,12 +75,6 @@ __device__ __forceinline__ void epilogue_linear(const typename Mma<E>::acc_t (&a
       }
     }
   }
-}
-
-template <Out O, class V>
-__device__ __forceinline__ void put_out_global(char* p, V v) {
-  if constexpr (O == Out::I32) *reinterpret_cast<int32_t*>(p) = v;
-  else *reinterpret_cast<float*>(p) = v;
 }
 
 // SwiGLU epilogue: tile column blocks alternate gate (even) and up (odd), so
@@ -124,6 +124,7 @@ struct ChunkedArgs {
   uint32_t epoch;
 };
 
+// Tile column -> global column of B, clamped to the last 16-byte column block.
 struct PlainCols {
   int64_t col0, last_block;
   __device__ __forceinline__ int64_t operator()(int j) const {
@@ -135,11 +136,15 @@ struct PlainCols {
 template <class TS, int OS>
 constexpr int chunked_smem() {
   // 32-bit outputs are not staged through LDS
-  return (OS == 4 || 2 * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
-             ? 2 * TS::kStageBytes
+  return (OS == 4 || TS::kStages * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
+             ? TS::kStages * TS::kStageBytes
              : TS::BM * (TS::BN * OS + 16);
 }
 
+// One workgroup per output tile. Tiles are numbered chunk by chunk in the
+// order the chunks are due (first_chunk, first_chunk + 1, ... mod W), and
+// inside a chunk column-block by column-block, so that the tiles running at
+// the same time share B columns and the chunks complete roughly in order.
 template <Elem E, bool BT, class TS, Out O>
 __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
   constexpr int OS = OutInfo<O>::bytes;
@@ -159,90 +164,19 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
 
   typename Mma<E>::acc_t acc[TS::FM][TS::FN];
   BDesc bd{p.B, p.ldb, p.n};
-  constexpr int CPB = 16 / ElemInfo<E>::bytes;
-  PlainCols cm{col0, p.n - CPB};
+  PlainCols cm{col0, p.n - 16 / ElemInfo<E>::bytes};
   mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
 
   if constexpr (OS == 2) {
     // 16-bit outputs: stage the tile in LDS, then 16-byte coalesced stores.
     constexpr int pitch = TS::BN * OS + 16;
     epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
-                              [&](int r, int c, float v) { put_out<O>(smem + r * pitch + c * OS, v); });
-    __syncthreads();
-    store_staged<TS::BM>(smem, pitch, TS::BN * OS, p.out + row0 * p.ldo, p.ldo, row_end - row0,
-                         col0 * OS, p.n * OS);
-  } else {
-    // 32-bit test outputs: stored straight from the accumulator layout.
-    char* base = p.out + row0 * p.ldo + col0 * OS;
-    const int64_t nrows = row_end - row0, ncols = p.n - col0;
-    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
-                              [&](int r, int c, auto v) {
-                                if (r < nrows && c < ncols) put_out_global<O>(base + r * p.ldo + c * OS, v);
-                              });
-  }
-
-  if (p.flags) {
-    // The workgroup barrier makes every wave's stores of this tile visible to
-    // thread 0, whose agent-scope release (one L2 write-back per tile) then
-    // covers them before the tile is counted. Only the last tile of a chunk
-    // acquires the other tiles' releases (an acquire invalidates this XCD's
-    // L2, so it is kept off the other tiles) and then publishes the epoch with
-    // a system-scope release store. Each wave first waits for its own stores
-    // to complete, so the write-back issued after the barrier sees them all.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t prev =
-          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev + 1 == static_cast<uint32_t>(p.tiles_per_chunk)) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-    }
-  }
-}
-
-// Eight-wave variant for 16-bit inputs (see gemm8.hpp); same schedule,
-// epilogue and ready-flag protocol as chunked_gemm_kernel.
-template <class TS, int OS>
-constexpr int chunked8_smem() {
-  return (OS == 4 || TS::kStages * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
-             ? TS::kStages * TS::kStageBytes
-             : TS::BM * (TS::BN * OS + 16);
-}
-
-template <Elem E, bool BT, class TS, Out O>
-__global__ __launch_bounds__(kThreads8, 1) void chunked_gemm8_kernel(ChunkedArgs p) {
-  constexpr int OS = OutInfo<O>::bytes;
-  constexpr int kSmem = chunked8_smem<TS, OS>();
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
-  lds_t* smem = (lds_t*)smem_raw;
-
-  const int b = blockIdx.x;
-  const int seq = b / p.tiles_per_chunk;
-  const int t = b - seq * p.tiles_per_chunk;
-  int c = p.first_chunk + seq;
-  c = c >= p.world ? c - p.world : c;
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
-  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * TS::BM;
-  const int64_t row_end = c * p.mc + p.mc;
-  const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
-
-  f32x4_t acc[TS::FM][TS::FN];
-  BDesc bd{p.B, p.ldb, p.n};
-  PlainCols cm{col0, p.n - 8};
-  mainloop8<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
-
-  if constexpr (OS == 2) {
-    constexpr int pitch = TS::BN * OS + 16;
-    epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
                               [&](int r, int cc, float v) { put_out<O>(smem + r * pitch + cc * OS, v); });
     __syncthreads();
-    store_staged8(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo, row_end - row0,
-                  col0 * OS, p.n * OS);
+    store_staged(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo, row_end - row0,
+                 col0 * OS, p.n * OS);
   } else {
+    // 32-bit test outputs: stored straight from the accumulator layout.
     char* base = p.out + row0 * p.ldo + col0 * OS;
     const int64_t nrows = row_end - row0, ncols = p.n - col0;
     epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
@@ -252,6 +186,12 @@ __global__ __launch_bounds__(kThreads8, 1) void chunked_gemm8_kernel(ChunkedArgs
   }
 
   if (p.flags) {
+    // Each wave waits for its own stores; after the barrier, thread 0's
+    // agent-scope release (one L2 write-back per tile) covers the whole tile
+    // before the tile is counted. Only the last tile of a chunk acquires the
+    // other tiles' releases (an acquire invalidates this XCD's L2, so it is
+    // kept off the other tiles) and then publishes the epoch with a
+    // system-scope release store.
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -306,11 +246,13 @@ struct GluCols {
 
 template <class TS, bool GLU>
 constexpr int grouped_smem() {
-  return (2 * TS::kStageBytes) > (TS::BM * ((GLU ? TS::BN / 2 : TS::BN) * 2 + 16))
-             ? 2 * TS::kStageBytes
+  return (TS::kStages * TS::kStageBytes) > (TS::BM * ((GLU ? TS::BN / 2 : TS::BN) * 2 + 16))
+             ? TS::kStages * TS::kStageBytes
              : TS::BM * ((GLU ? TS::BN / 2 : TS::BN) * 2 + 16);
 }
 
+// Persistent grouped GEMM: every workgroup derives the tile -> (expert, rows,
+// columns) map from the device-side counts, so the host never reads them.
 template <class TS, bool GLU>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
   constexpr int kSmem = grouped_smem<TS, GLU>();
@@ -327,7 +269,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
   constexpr int OUTC = GLU ? TS::BN / 2 : TS::BN;  // output columns per tile
   const int64_t tiles_n = (p.n_out + OUTC - 1) / OUTC;
 
-  // Counts -> group table, computed by every workgroup from device memory.
+  // Counts -> group table.
   if (tid == 0) { s_base = 0; s_bad = 0; }
   __syncthreads();
   int64_t part = 0;
@@ -397,63 +339,49 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
           acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
           [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
     __syncthreads();
-    store_staged<TS::BM>(smem, pitch, OUTC * 2, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
-                         ocol0 * 2, p.n_out * 2);
+    store_staged(smem, pitch, OUTC * 2, TS::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
+                 ocol0 * 2, p.n_out * 2);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- host side
 
-#ifndef MC2_MAIN_BM
-#define MC2_MAIN_BM 128
-#endif
-using TileMain = TileShape<MC2_MAIN_BM, 256, 2, 2>;
+using TileL = Tile<256, 256, 2, 4>;  // wave sub-tile 128 x 64
+using TileM = Tile<128, 256, 2, 4>;  // wave sub-tile 64 x 64, for small tile counts
 
-#ifndef MC2_T8_KR
-#define MC2_T8_KR 128
-#define MC2_T8_S 2
-#endif
-using Tile16 = Tile8<256, 256, 2, 4, MC2_T8_KR, MC2_T8_S>;
-
-template <Elem E> struct TileFor { using type = TileMain; };
-template <> struct TileFor<Elem::F16> { using type = Tile16; };
-template <> struct TileFor<Elem::BF16> { using type = Tile16; };
-
-template <Elem E, bool BT, Out O>
+template <Elem E, bool BT, class TS, Out O>
 static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s) {
-  if constexpr (E == Elem::I8)
-    hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TileMain, O>), dim3(blocks), dim3(kThreads), 0,
-                       s, a);
-  else
-    hipLaunchKernelGGL((chunked_gemm8_kernel<E, BT, Tile16, O>), dim3(blocks), dim3(kThreads8), 0,
-                       s, a);
+  hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TS, O>), dim3(blocks), dim3(kThreads), 0, s, a);
   return hipGetLastError();
-}
-
-template <Elem E, bool BT>
-static hipError_t launch_chunked_out(const ChunkedArgs& a, int out_dtype, int blocks,
-                                     hipStream_t s) {
-  switch (out_dtype) {
-    case MC2_BF16: return launch_chunked<E, BT, Out::BF16>(a, blocks, s);
-    case MC2_F16: return launch_chunked<E, BT, Out::F16>(a, blocks, s);
-    case MC2_F32: return launch_chunked<E, BT, Out::F32>(a, blocks, s);
-    default: return launch_chunked<E, BT, Out::I32>(a, blocks, s);
-  }
 }
 
 // Instantiated combinations: F16 -> {F16, F32}; BF16 -> {BF16, F32};
 // I8 -> {BF16, F16, F32, I32}.
-template <bool BT>
+template <bool BT, class TS>
 static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArgs& a, int blocks,
                                    hipStream_t s) {
   if (in_dtype == MC2_F16)
-    return out_dtype == MC2_F32 ? launch_chunked<Elem::F16, BT, Out::F32>(a, blocks, s)
-                                : launch_chunked<Elem::F16, BT, Out::F16>(a, blocks, s);
+    return out_dtype == MC2_F32 ? launch_chunked<Elem::F16, BT, TS, Out::F32>(a, blocks, s)
+                                : launch_chunked<Elem::F16, BT, TS, Out::F16>(a, blocks, s);
   if (in_dtype == MC2_BF16)
-    return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, Out::F32>(a, blocks, s)
-                                : launch_chunked<Elem::BF16, BT, Out::BF16>(a, blocks, s);
-  return launch_chunked_out<Elem::I8, BT>(a, out_dtype, blocks, s);
+    return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
+                                : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
+  switch (out_dtype) {
+    case MC2_BF16: return launch_chunked<Elem::I8, BT, TS, Out::BF16>(a, blocks, s);
+    case MC2_F16: return launch_chunked<Elem::I8, BT, TS, Out::F16>(a, blocks, s);
+    case MC2_F32: return launch_chunked<Elem::I8, BT, TS, Out::F32>(a, blocks, s);
+    default: return launch_chunked<Elem::I8, BT, TS, Out::I32>(a, blocks, s);
+  }
+}
+
+// Tile height for a problem: 256-row tiles unless they leave too much of the
+// GPU idle in the last wave of tiles, then 128-row tiles.
+static bool use_tall_tiles(int64_t mc, int64_t n, int W) {
+  const int64_t cus = num_cus();
+  const int64_t tiles = ((mc + 255) / 256) * ((n + 255) / 256) * W;
+  const int64_t waves = (tiles + cus - 1) / cus;
+  return tiles * 10 >= waves * cus * 8;  // >= 80% of the slots busy
 }
 
 static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
@@ -474,9 +402,7 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.lda = k * es;
   a.ldb = (x2_trans ? k : n) * es;
   a.ldo = n * os;
-  // K values per main-loop stage: 32 in the eight-wave 16-bit loop, 128 bytes
-  // of int8 in the four-wave loop.
-  const int ke = in_dtype == MC2_I8 ? kKBytes : Tile16::kKE;
+  const int ke = kKBytes / es;  // K values per main-loop stage
   a.ks.k = k;
   a.ks.a_shard = m * k * es;
   a.ks.b_shard = k * n * es;
@@ -485,10 +411,10 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.mc = m / W;
   a.world = W;
   a.first_chunk = first_chunk;
-  const int BM = in_dtype == MC2_I8 ? TileMain::BM : Tile16::BM;
-  const int BN = in_dtype == MC2_I8 ? TileMain::BN : Tile16::BN;
+  const bool tall = use_tall_tiles(a.mc, n, W);
+  const int BM = tall ? TileL::BM : TileM::BM;
   a.tiles_m = static_cast<int>((a.mc + BM - 1) / BM);
-  a.tiles_n = static_cast<int>((n + BN - 1) / BN);
+  a.tiles_n = static_cast<int>((n + 255) / 256);
   a.tiles_per_chunk = a.tiles_m * a.tiles_n;
   a.bias_mul = static_cast<float>(nsim);
   a.flags = flags;
@@ -496,12 +422,23 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.epoch = epoch;
   const int64_t blocks = static_cast<int64_t>(a.tiles_per_chunk) * W;
   if (blocks > 0x7fffffff) return MC2_ERR_SHAPE;
-  hipError_t e = x2_trans ? dispatch_chunked<true>(in_dtype, out_dtype, a, (int)blocks, stream)
-                          : dispatch_chunked<false>(in_dtype, out_dtype, a, (int)blocks, stream);
+  hipError_t e;
+  if (tall)
+    e = x2_trans ? dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)
+                 : dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
+  else
+    e = x2_trans ? dispatch_chunked<true, TileM>(in_dtype, out_dtype, a, (int)blocks, stream)
+                 : dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
   return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 
 static bool valid_world(int W) { return W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32; }
+
+// Per-lane buffer offsets are 32-bit: rows of up to 256 (A, B given as (n, k))
+// or 128 (row-major B) per tile must stay below 2^31 bytes.
+static bool offsets_fit(int64_t lda, int64_t ldb) {
+  return lda * 256 < 0x7fff0000LL && ldb * 256 < 0x7fff0000LL;
+}
 
 }  // namespace mc2
 
@@ -535,6 +472,8 @@ extern "C" int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_
     if (k % 8 || n % 8) return MC2_ERR_ALIGN;
   }
   if (!aligned16(x1) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
+  const int es = quant ? 1 : 2;
+  if (!offsets_fit(k * es, (x2_trans ? k : n) * es)) return MC2_ERR_UNSUPPORTED;
   if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
   if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
   const int first = (rank + 1) % world_size;
@@ -552,6 +491,7 @@ extern "C" int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m
   if (in_dtype != MC2_F16 && in_dtype != MC2_BF16) return MC2_ERR_DTYPE;
   if (k % 8 || n % 8) return MC2_ERR_ALIGN;
   if (!aligned16(x_gathered) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
+  if (!offsets_fit(k * 2, (x2_trans ? k : n) * 2)) return MC2_ERR_UNSUPPORTED;
   if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
   if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
   return run_chunked(x_gathered, x2, m_c * world_size, k, n, world_size, rank, 1, x2_trans,
@@ -563,17 +503,16 @@ extern "C" int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m
 
 namespace mc2 {
 
-using TileGroup = TileShape<128, 256, 2, 2>;
+using TileG = TileL;
 
 static int run_grouped(bool glu, const GroupedArgs& a, int64_t max_tiles, hipStream_t stream) {
   const int64_t grid64 = max_tiles < num_cus() ? max_tiles : num_cus();
   const int grid = static_cast<int>(grid64 > 0 ? grid64 : 1);
   if (glu)
-    hipLaunchKernelGGL((grouped_gemm_kernel<TileGroup, true>), dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<TileG, true>), dim3(grid), dim3(kThreads), 0, stream, a);
   else
-    hipLaunchKernelGGL((grouped_gemm_kernel<TileGroup, false>), dim3(grid), dim3(kThreads), 0,
-                       stream, a);
+    hipLaunchKernelGGL((grouped_gemm_kernel<TileG, false>), dim3(grid), dim3(kThreads), 0, stream,
+                       a);
   return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 
@@ -599,6 +538,7 @@ extern "C" int mc2_gmm_dispatch(const void* send_buf, int64_t send_rows, const i
   if (act != MC2_ACT_NONE && act != MC2_ACT_SWIGLU) return MC2_ERR_SHAPE;
   if (H % 8 || I2 % 16) return MC2_ERR_ALIGN;
   if (!aligned16(send_buf) || !aligned16(w1) || !aligned16(h_out)) return MC2_ERR_ALIGN;
+  if (!offsets_fit(H * 2, I2 * 2)) return MC2_ERR_UNSUPPORTED;
   const bool glu = act == MC2_ACT_SWIGLU;
   GroupedArgs a{};
   a.A = static_cast<const char*>(send_buf);
@@ -622,9 +562,9 @@ extern "C" int mc2_gmm_dispatch(const void* send_buf, int64_t send_rows, const i
   a.o_cap = h_rows;
   a.dev_err = dev_err;
   a.ktiles = static_cast<int>((H + 63) / 64);
-  const int outc = glu ? TileGroup::BN / 2 : TileGroup::BN;
+  const int outc = glu ? TileG::BN / 2 : TileG::BN;
   const int64_t rows = send_rows < h_rows ? send_rows : h_rows;
-  const int64_t max_tiles = (rows / TileGroup::BM + local_experts) * ((a.n_out + outc - 1) / outc);
+  const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((a.n_out + outc - 1) / outc);
   return run_grouped(glu, a, max_tiles, stream);
 }
 
@@ -639,6 +579,7 @@ extern "C" int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* rec
   if (I < 1 || H < 8 || h_rows < 0 || combine_rows < 0) return MC2_ERR_SHAPE;
   if (I % 8 || H % 8) return MC2_ERR_ALIGN;
   if (!aligned16(h) || !aligned16(w2) || !aligned16(combine_buf)) return MC2_ERR_ALIGN;
+  if (!offsets_fit(I * 2, H * 2)) return MC2_ERR_UNSUPPORTED;
   GroupedArgs a{};
   a.A = static_cast<const char*>(h);
   a.lda = I * 2;
@@ -663,6 +604,6 @@ extern "C" int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* rec
   a.ktiles = static_cast<int>((I + 63) / 64);
   const int64_t rows = h_rows < combine_rows ? h_rows : combine_rows;
   const int64_t max_tiles =
-      (rows / TileGroup::BM + local_experts) * ((H + TileGroup::BN - 1) / TileGroup::BN);
+      (rows / TileG::BM + local_experts) * ((H + TileG::BN - 1) / TileG::BN);
   return run_grouped(false, a, max_tiles, stream);
 }
