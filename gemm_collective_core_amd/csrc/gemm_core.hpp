@@ -6,12 +6,25 @@
 // and the per-CU load rate is what bounds a GEMM tile on this chip.
 //
 // K advances in stages of 128 bytes per row (64 bf16/fp16 or 128 int8
-// values) held in a two-buffer LDS ring. Loads go straight from global memory
-// to LDS (buffer loads with the LDS bit): no staging registers, and lanes
-// whose offset lies past the buffer's range write zeros, which pads the K
-// tail. The loads of stage i+1 are issued right after the barrier that
-// publishes stage i and overlap its MFMAs; each wave then waits only for its
-// own loads (vmcnt) before the next barrier.
+// values, two MFMA k-steps) held in a two-buffer LDS ring. Loads go straight
+// from global memory to LDS (buffer loads with the LDS bit): no staging
+// registers, and lanes whose offset lies past the buffer's range write zeros,
+// which pads the K tail.
+//
+// Software pipeline of one stage, per wave (rows = the wave's FM fragment
+// rows of 16):
+//   k-step 0: row by row, the MFMAs of the row, then the LDS reads of the
+//             same row for k-step 1 (B fragments of k-step 1 after row 0);
+//   k-step 1: rows 0..S0; then the stage barrier (all reads of this stage
+//             done, every wave's loads of the next stage landed), then the
+//             reads of the next stage's k-step 0 and, spread over the
+//             remaining rows, the loads of the stage after next into the
+//             buffer just released.
+// So operand reads overlap MFMAs instead of preceding them, and a wave never
+// issues a burst of loads: a load instruction stalls its wave until the
+// memory pipeline takes it, which in a burst would idle the MFMA unit. Every
+// LDS read is inline assembly and waited for with explicit lgkmcnt values
+// (LDS returns in order); the compiler does not track these reads.
 //
 // MFMA shapes: v_mfma_f32_16x16x32_{bf16,f16} and v_mfma_i32_16x16x64_i8.
 // Lane l supplies row (l & 15) of A and column (l & 15) of B; the four lane
@@ -20,9 +33,13 @@
 //
 // LDS layouts (per stage):
 //  * A (m, k), and B given as (n, k): one 128-byte row per output row /
-//    column, K contiguous; 16-byte chunk c of row r at c ^ ((r ^ (r >> 3)) & 7)
-//    so that an operand read (16 rows, one chunk) and a load (8 rows, all
-//    chunks) both spread over all banks.
+//    column, K contiguous; 16-byte chunk c of row r at c ^ ((r >> 1) & 7).
+//    The LDS has 64 four-byte banks (256 bytes), so rows r and r + 1 fall on
+//    different bank halves; an operand read (16 rows, one logical chunk) then
+//    puts the 8 even and the 8 odd rows on 8 distinct chunks each, and never
+//    conflicts. Loads write 1 KiB linearly and never conflict either. The
+//    swizzle does not depend on the fragment index (rows 16 apart), so all
+//    fragment reads of a wave share one address register per k-step.
 //  * B given row-major as (k, n): kept k-major as loaded (rows of BN
 //    elements). Operands come from the transposing LDS reads: within a 16-lane
 //    group, ds_read_b64_tr_b16 hands lane i element i mod 4 of the 8-byte
@@ -100,7 +117,7 @@ struct BDesc {
 };
 
 __device__ __forceinline__ int row_off(int r, int c) {
-  return r * kKBytes + ((c ^ ((r ^ (r >> 3)) & 7)) << 4);
+  return r * kKBytes + ((c ^ ((r >> 1) & 7)) << 4);
 }
 
 // k-major swizzles: 16-bit rows (512 bytes) move 32-byte pairs, 8-bit rows
@@ -108,71 +125,109 @@ __device__ __forceinline__ int row_off(int r, int c) {
 __device__ __forceinline__ int kmaj_swz16(int kr) { return (kr & 3) | (((kr >> 3) & 1) << 2); }
 __device__ __forceinline__ int kmaj_swz8(int kr) { return (kr & 7) | (((kr >> 4) & 1) << 3); }
 
-// Waits for all outstanding LDS reads; the fragments are tied to the wait so
-// that no instruction using them is scheduled before it.
-template <int N>
-__device__ __forceinline__ void lds_wait_tied(u32x4_t (&v)[N]) {
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(v[i]));
+// Waits until at most n LDS operations of this wave are outstanding (n is a
+// compile-time constant after unrolling; values above 15, the counter's
+// range, wait for 15).
+__device__ __forceinline__ void lgkm_wait(int n) {
+  switch (n < 15 ? n : 15) {
+    case 0: asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); break;
+    case 1: asm volatile("s_waitcnt lgkmcnt(1)" ::: "memory"); break;
+    case 2: asm volatile("s_waitcnt lgkmcnt(2)" ::: "memory"); break;
+    case 3: asm volatile("s_waitcnt lgkmcnt(3)" ::: "memory"); break;
+    case 4: asm volatile("s_waitcnt lgkmcnt(4)" ::: "memory"); break;
+    case 5: asm volatile("s_waitcnt lgkmcnt(5)" ::: "memory"); break;
+    case 6: asm volatile("s_waitcnt lgkmcnt(6)" ::: "memory"); break;
+    case 7: asm volatile("s_waitcnt lgkmcnt(7)" ::: "memory"); break;
+    case 8: asm volatile("s_waitcnt lgkmcnt(8)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt lgkmcnt(9)" ::: "memory"); break;
+    case 10: asm volatile("s_waitcnt lgkmcnt(10)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt lgkmcnt(11)" ::: "memory"); break;
+    case 12: asm volatile("s_waitcnt lgkmcnt(12)" ::: "memory"); break;
+    case 13: asm volatile("s_waitcnt lgkmcnt(13)" ::: "memory"); break;
+    case 14: asm volatile("s_waitcnt lgkmcnt(14)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt lgkmcnt(15)" ::: "memory"); break;
+  }
 }
 
-// B operand of one 16-column block from the k-major layout for k-step ks.
-// The transposing reads are inline assembly: the compiler cannot tell that
-// they do not overlap the LDS stage still being filled by in-flight loads and
-// would otherwise wait for those. Results are consumed after lds_wait_tied().
+// 16-byte operand read; the value is valid only after a matching lgkm_wait.
+__device__ __forceinline__ u32x4_t lds_rd128(const lds_t* p) {
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1"
+               : "=v"(v)
+               : "v"(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)))
+               : "memory");
+  return v;
+}
+
+// Half h (k rows 4h.. of each lane group) of the B operand of the 16-column
+// block at n0 for k-step ks, from the k-major layout: a transposing read, 8
+// bytes per lane; valid after a matching lgkm_wait.
 template <Elem E>
-__device__ __forceinline__ u32x4_t read_b_kmaj(const lds_t* lB, int ks, int n0, int lane) {
+__device__ __forceinline__ u32x2_t lds_rd_tr(const lds_t* lB, int ks, int n0, int h, int lane) {
   const int g = lane >> 4, j = lane & 15;
-  u32x4_t out;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    int off;
-    if constexpr (ElemInfo<E>::bytes == 2) {
-      const int kr = ks * 32 + g * 8 + h * 4 + (j >> 2);
-      off = kr * 512 + (((n0 >> 4) ^ kmaj_swz16(kr)) << 5) + ((j & 3) << 3);
-    } else {
-      const int kr = ks * 64 + g * 16 + h * 8 + (j >> 1);
-      off = kr * 256 + (((n0 >> 4) ^ kmaj_swz8(kr)) << 4) + ((j & 1) << 3);
-    }
-    const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lB + off));
-    u32x2_t w;
-    if constexpr (ElemInfo<E>::bytes == 2)
-      asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr));
-    else
-      asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(w) : "v"(addr));
-    out[2 * h] = w[0];
-    out[2 * h + 1] = w[1];
+  int off;
+  if constexpr (ElemInfo<E>::bytes == 2) {
+    const int kr = ks * 32 + g * 8 + h * 4 + (j >> 2);
+    off = kr * 512 + (((n0 >> 4) ^ kmaj_swz16(kr)) << 5) + ((j & 3) << 3);
+  } else {
+    const int kr = ks * 64 + g * 16 + h * 8 + (j >> 1);
+    off = kr * 256 + (((n0 >> 4) ^ kmaj_swz8(kr)) << 4) + ((j & 1) << 3);
   }
-  return out;
+  const uint32_t addr = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(lB + off));
+  u32x2_t w;
+  if constexpr (ElemInfo<E>::bytes == 2)
+    asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(w) : "v"(addr) : "memory");
+  else
+    asm volatile("ds_read_b64_tr_b8 %0, %1" : "=v"(w) : "v"(addr) : "memory");
+  return w;
 }
 
-// MFMAs of one K stage (two k-steps) on the wave's FM x FN fragments.
-template <Elem E, class TS, bool BT>
-__device__ __forceinline__ void mma_stage(const lds_t* lA, const lds_t* lB,
-                                          typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
-                                          int wrow0, int wcol0, int lane) {
+// B operand registers of one k-step. B given as (n, k) keeps whole fragments;
+// row-major B keeps the two 8-byte halves the transposing reads return, and
+// the 16-byte MFMA operand is formed where it is used, after the wait, so
+// that no register copy can read a half still in flight.
+template <bool BT, int FN> struct BRegs;
+template <int FN> struct BRegs<true, FN> {
+  static constexpr int kOps = FN;  // LDS reads per k-step
+  u32x4_t q[FN];
+  __device__ __forceinline__ void tie() {
 #pragma unroll
-  for (int ks = 0; ks < 2; ++ks) {
-    const int ch = ks * 4 + (lane >> 4);
-    u32x4_t a[TS::FM], b[TS::FN];
-#pragma unroll
-    for (int fn = 0; fn < TS::FN; ++fn) {
-      if constexpr (BT)
-        b[fn] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lB + row_off(wcol0 + fn * 16 + (lane & 15), ch));
-      else
-        b[fn] = read_b_kmaj<E>(lB, ks, wcol0 + fn * 16, lane);
-    }
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm)
-      a[fm] = *reinterpret_cast<const MC2_LDS u32x4_t*>(lA + row_off(wrow0 + fm * 16 + (lane & 15), ch));
-    if constexpr (!BT) lds_wait_tied(b);
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < TS::FN; ++fn)
-        acc[fm][fn] = Mma<E>::run(a[fm], b[fn], acc[fm][fn]);
+    for (int i = 0; i < FN; ++i) asm volatile("" : "+v"(q[i]));
   }
+  __device__ __forceinline__ u32x4_t get(int fn) const { return q[fn]; }
+};
+template <int FN> struct BRegs<false, FN> {
+  static constexpr int kOps = 2 * FN;
+  u32x2_t h[FN][2];
+  __device__ __forceinline__ void tie() {
+#pragma unroll
+    for (int i = 0; i < FN; ++i) {
+      asm volatile("" : "+v"(h[i][0]));
+      asm volatile("" : "+v"(h[i][1]));
+    }
+  }
+  __device__ __forceinline__ u32x4_t get(int fn) const {
+    return u32x4_t{h[fn][0][0], h[fn][0][1], h[fn][1][0], h[fn][1][1]};
+  }
+};
+
+template <Elem E, bool BT, class TS>
+__device__ __forceinline__ void read_b_all(BRegs<BT, TS::FN>& b, const lds_t* lB, int ks, int wcol0,
+                                           int lane) {
+#pragma unroll
+  for (int fn = 0; fn < TS::FN; ++fn) {
+    if constexpr (BT) {
+      b.q[fn] = lds_rd128(lB + row_off(wcol0 + fn * 16 + (lane & 15), ks * 4 + (lane >> 4)));
+    } else {
+      b.h[fn][0] = lds_rd_tr<E>(lB, ks, wcol0 + fn * 16, 0, lane);
+      b.h[fn][1] = lds_rd_tr<E>(lB, ks, wcol0 + fn * 16, 1, lane);
+    }
+  }
+}
+
+template <class TS>
+__device__ __forceinline__ u32x4_t read_a(const lds_t* lA, int fm, int ks, int wrow0, int lane) {
+  return lds_rd128(lA + row_off(wrow0 + fm * 16 + (lane & 15), ks * 4 + (lane >> 4)));
 }
 
 constexpr uint32_t kBufFlags = 0x00020000u;  // raw buffer, 32-bit data format
@@ -199,7 +254,7 @@ __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)
 // column block, clamped to the matrix). Every load instruction moves 1 KiB:
 // 8 rows of 128 bytes for A and for B given as (n, k); 2 (16-bit) or 4
 // (8-bit) k rows of 256 columns for row-major B. Each wave issues BM/64 A
-// loads and 4 B loads per stage.
+// loads and 4 B loads per stage. The schedule is described at the top.
 template <Elem E, bool BT, class TS, class ColMap>
 __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                          int64_t row_last, const BDesc& B, int64_t col0,
@@ -259,39 +314,118 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
   const char* a_base = A + row0 * lda;
   const char* b_base = BT ? B.base + col0 * B.ld : B.base;
 
-  auto issue = [&](int it) {
+  // Loads of stage `it`: the buffer resources are formed once (prep) and the
+  // NA + NB instructions issued one by one (issue_j) between MFMA rows.
+  struct StageLd {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int64_t kleft;  // K values left in this shard
+    lds_t* st;
+  };
+  auto prep = [&](int it) {
+    StageLd s;
     const int w = it / ks.ktiles;
     const int kt = it - w * ks.ktiles;
     const int64_t kdone = static_cast<int64_t>(kt) * KE;
-    const int64_t kleft = ks.k - kdone;  // K values left in this shard
-    lds_t* st = smem + (it & 1) * TS::kStageBytes;
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + w * ks.a_shard + kdone * ES);
-#pragma unroll
-    for (int j = 0; j < NA; ++j)
-      dma16(ra, st + 8 * (NA * wave + j) * kKBytes, a_key[j] < kleft ? a_off[j] : kOffNone);
-    if constexpr (BT) {
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * ES);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        dma16(rb, st + TS::kABytes + 8 * (NB * wave + j) * kKBytes,
-              b_key[j] < kleft ? b_off[j] : kOffNone);
+    s.kleft = ks.k - kdone;
+    s.st = smem + (it & 1) * TS::kStageBytes;
+    s.ra = make_rsrc(a_base + w * ks.a_shard + kdone * ES);
+    s.rb = BT ? make_rsrc(b_base + w * ks.b_shard + kdone * ES)
+              : make_rsrc(b_base + w * ks.b_shard + kdone * B.ld);
+    return s;
+  };
+  auto issue_j = [&](const StageLd& s, int j) {
+    if (j < NA) {
+      dma16(s.ra, s.st + 8 * (NA * wave + j) * kKBytes, a_key[j] < s.kleft ? a_off[j] : kOffNone);
+    } else if constexpr (BT) {
+      const int jb = j - NA;
+      dma16(s.rb, s.st + TS::kABytes + 8 * (NB * wave + jb) * kKBytes,
+            b_key[jb] < s.kleft ? b_off[jb] : kOffNone);
     } else {
-      const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + w * ks.b_shard + kdone * B.ld);
-#pragma unroll
-      for (int j = 0; j < NB; ++j)
-        dma16(rb, st + TS::kABytes + KRI * (NB * wave + j) * (TS::BN * ES),
-              b_key[j] < kleft ? b_off[j] : kOffNone);
+      const int jb = j - NA;
+      dma16(s.rb, s.st + TS::kABytes + KRI * (NB * wave + jb) * (TS::BN * ES),
+            b_key[jb] < s.kleft ? b_off[jb] : kOffNone);
     }
+  };
+  auto issue_all = [&](int it) {
+    const StageLd s = prep(it);
+#pragma unroll
+    for (int j = 0; j < NA + NB; ++j) issue_j(s, j);
   };
 
   const int n = ks.niters;
-  issue(0);
+  constexpr int FM = TS::FM, FN = TS::FN;
+  constexpr int NBO = BRegs<BT, FN>::kOps;
+  constexpr int S0 = FM / 2 - 1;                  // k-step-1 row followed by the barrier
+  constexpr int NL = NA + NB;                     // loads per wave per stage
+  constexpr int LROWS = FM - 1 - S0;              // k-step-1 rows that carry them
+  constexpr int LPER = (NL + LROWS - 1) / LROWS;  // loads per row
+  static_assert(NL <= 15, "vmcnt range of the prologue");
+  u32x4_t a[FM];  // row fm's A fragment, refilled once the row's MFMAs are issued
+  BRegs<BT, FN> b0, b1;
+  StageLd nx;     // loads of the stage after next
+  if (n > 0) {
+    issue_all(0);
+    if (n > 1) {
+      issue_all(1);
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");  // stage 0 has landed
+    } else {
+      wait_vmcnt0();
+    }
+    bar_sync();
+    read_b_all<E, BT, TS>(b0, smem + TS::kABytes, 0, wcol0, lane);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) a[fm] = read_a<TS>(smem, fm, 0, wrow0, lane);
+  }
+  // LDS reads in flight at each wait, in issue order: at k-step-0 row fm, the
+  // A reads of rows > fm, then the k-step-1 reads issued so far (NBO B reads
+  // and one A read at row 0, one more A read per row after that); at
+  // k-step-1 row fm <= S0, the A reads of rows > fm.
   for (int it = 0; it < n; ++it) {
-    wait_vmcnt0();  // this wave's loads of stage `it` have landed
-    bar_sync();     // ... and every wave's; stage it-1 is no longer read
-    if (it + 1 < n) issue(it + 1);
     const lds_t* cur = smem + (it & 1) * TS::kStageBytes;
-    mma_stage<E, TS, BT>(cur, cur + TS::kABytes, acc, wrow0, wcol0, lane);
+    const lds_t* nxt = smem + ((it + 1) & 1) * TS::kStageBytes;
+    const bool more = it + 1 < n;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      lgkm_wait(FM - 1 - fm + (fm == 0 ? 0 : NBO + fm));
+      asm volatile("" : "+v"(a[fm]));
+      if (fm == 0) b0.tie();
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = Mma<E>::run(a[fm], b0.get(fn), acc[fm][fn]);
+      if (fm == 0) read_b_all<E, BT, TS>(b1, cur + TS::kABytes, 1, wcol0, lane);
+      a[fm] = read_a<TS>(cur, fm, 1, wrow0, lane);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      if (fm <= S0) {
+        lgkm_wait(FM - 1 - fm);
+        asm volatile("" : "+v"(a[fm]));
+        if (fm == 0) b1.tie();
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = Mma<E>::run(a[fm], b1.get(fn), acc[fm][fn]);
+      if (fm > S0 && it + 2 < n) {
+#pragma unroll
+        for (int q = 0; q < LPER; ++q) {
+          const int j = (fm - S0 - 1) * LPER + q;
+          if (j < NL) issue_j(nx, j);
+        }
+      }
+      if (fm == S0) {
+        lgkm_wait(0);   // every read of this stage is done
+        wait_vmcnt0();  // this wave's loads of the next stage have landed
+        bar_sync();     // ... and every wave's
+        if (it + 2 < n) nx = prep(it + 2);
+        if (more) {
+          read_b_all<E, BT, TS>(b0, nxt + TS::kABytes, 0, wcol0, lane);
+#pragma unroll
+          for (int f = 0; f <= S0; ++f) a[f] = read_a<TS>(nxt, f, 0, wrow0, lane);
+        }
+      } else if (fm > S0 && more) {
+        a[fm] = read_a<TS>(nxt, fm, 0, wrow0, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   bar_sync();
 }

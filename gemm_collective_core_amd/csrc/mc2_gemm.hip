@@ -118,6 +118,7 @@ struct ChunkedArgs {
   int64_t mc;             // rows per chunk
   int world, first_chunk;
   int tiles_m, tiles_n, tiles_per_chunk;
+  int round;              // workgroups per dispatch round (CUs, multiple of 8); 0: no remap
   float bias_mul;
   uint32_t* flags;
   uint32_t* counters;
@@ -141,10 +142,21 @@ constexpr int chunked_smem() {
              : TS::BM * (TS::BN * OS + 16);
 }
 
+// Logical tile of workgroup b. Workgroups are dispatched to the 8 XCDs in
+// turn (b mod 8), each XCD with its own L2. Inside every round of `round`
+// workgroups (one per CU), XCD x is given the round's logical tiles
+// 32x .. 32x+31 (round/8 of them): consecutive tiles, which share rows of A
+// and columns of B, then run on the same L2.
+__device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
+  if (round <= 0 || b >= (nblocks / round) * round) return b;
+  const int r = b / round, u = b - r * round;
+  return r * round + (u & 7) * (round >> 3) + (u >> 3);
+}
+
 // One workgroup per output tile. Tiles are numbered chunk by chunk in the
 // order the chunks are due (first_chunk, first_chunk + 1, ... mod W), and
-// inside a chunk column-block by column-block, so that the tiles running at
-// the same time share B columns and the chunks complete roughly in order.
+// inside a chunk row-block fastest, so that a run of consecutive tiles forms a
+// compact block of the chunk and the chunks complete roughly in order.
 template <Elem E, bool BT, class TS, Out O>
 __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
   constexpr int OS = OutInfo<O>::bytes;
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   lds_t* smem = (lds_t*)smem_raw;
 
-  const int b = blockIdx.x;
+  const int b = xcd_tile(blockIdx.x, p.round, gridDim.x);
   const int seq = b / p.tiles_per_chunk;
   const int t = b - seq * p.tiles_per_chunk;
   int c = p.first_chunk + seq;
@@ -309,7 +321,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
   const int64_t total = s_tstart[El];
 
   KSpan ks{p.K, 0, 0, p.ktiles, p.ktiles};
-  for (int64_t t = blockIdx.x; t < total; t += gridDim.x) {
+  // With one workgroup per CU (a multiple of 8), XCD x takes tiles 32x ..
+  // 32x+31 of every round of the tile sequence (see xcd_tile).
+  const int g8 = gridDim.x;
+  const int64_t tfirst = (g8 % 8 == 0) ? (blockIdx.x & 7) * (g8 >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+  for (int64_t t = tfirst; t < total; t += gridDim.x) {
     int g = 0;
     while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
     const int64_t cnt = s_gstart[g + 1] - s_gstart[g];
@@ -376,12 +392,14 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
 }
 
 // Tile height for a problem: 256-row tiles unless they leave too much of the
-// GPU idle in the last wave of tiles, then 128-row tiles.
+// GPU idle in the last round of tiles, then 128-row tiles (measured on the
+// 8192 x 3072 x 3072 share: 256-row tiles at 75% occupancy of their two
+// rounds still beat 128-row tiles at 100% of three).
 static bool use_tall_tiles(int64_t mc, int64_t n, int W) {
   const int64_t cus = num_cus();
   const int64_t tiles = ((mc + 255) / 256) * ((n + 255) / 256) * W;
-  const int64_t waves = (tiles + cus - 1) / cus;
-  return tiles * 10 >= waves * cus * 8;  // >= 80% of the slots busy
+  const int64_t rounds = (tiles + cus - 1) / cus;
+  return tiles * 10 >= rounds * cus * 7;  // >= 70% of the slots busy
 }
 
 static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
@@ -416,6 +434,7 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.tiles_m = static_cast<int>((a.mc + BM - 1) / BM);
   a.tiles_n = static_cast<int>((n + 255) / 256);
   a.tiles_per_chunk = a.tiles_m * a.tiles_n;
+  a.round = static_cast<int>(num_cus() / 8 * 8);
   a.bias_mul = static_cast<float>(nsim);
   a.flags = flags;
   a.counters = counters;
