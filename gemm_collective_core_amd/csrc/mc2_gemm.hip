@@ -119,6 +119,7 @@ struct ChunkedArgs {
   int world, first_chunk;
   int tiles_m, tiles_n, tiles_per_chunk;
   int round;              // workgroups per dispatch round (CUs, multiple of 8); 0: no remap
+  int n_full;             // work units below n_full are whole tiles, the rest half tiles
   float bias_mul;
   uint32_t* flags;
   uint32_t* counters;
@@ -153,24 +154,24 @@ __device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
   return r * round + (u & 7) * (round >> 3) + (u >> 3);
 }
 
-// One workgroup per output tile. Tiles are numbered chunk by chunk in the
-// order the chunks are due (first_chunk, first_chunk + 1, ... mod W), and
-// inside a chunk row-block fastest, so that a run of consecutive tiles forms a
-// compact block of the chunk and the chunks complete roughly in order.
+// One output tile (or the row half `half` of one, for a TS of half height):
+// main loop, epilogue, store, and the chunk's ready flag. Tiles are numbered
+// chunk by chunk in the order the chunks are due (first_chunk,
+// first_chunk + 1, ... mod W), and inside a chunk row-block fastest, so that a
+// run of consecutive tiles forms a compact block of the chunk and the chunks
+// complete roughly in order. `weight` is the tile's share of the chunk
+// counter (2 for a whole tile, 1 for a half).
 template <Elem E, bool BT, class TS, Out O>
-__global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
+__device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, int tile, int half,
+                                             uint32_t weight) {
   constexpr int OS = OutInfo<O>::bytes;
-  constexpr int kSmem = chunked_smem<TS, OS>();
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
-  lds_t* smem = (lds_t*)smem_raw;
-
-  const int b = xcd_tile(blockIdx.x, p.round, gridDim.x);
-  const int seq = b / p.tiles_per_chunk;
-  const int t = b - seq * p.tiles_per_chunk;
+  const int seq = tile / p.tiles_per_chunk;
+  const int t = tile - seq * p.tiles_per_chunk;
   int c = p.first_chunk + seq;
   c = c >= p.world ? c - p.world : c;
   const int tm = t % p.tiles_m, tn = t / p.tiles_m;
-  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * TS::BM;
+  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * (TS::BM << (weight == 1)) +
+                       static_cast<int64_t>(half) * TS::BM;
   const int64_t row_end = c * p.mc + p.mc;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
 
@@ -208,15 +209,37 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
     __syncthreads();
     if (threadIdx.x == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t prev =
-          __hip_atomic_fetch_add(&p.counters[c], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (prev + 1 == static_cast<uint32_t>(p.tiles_per_chunk)) {
+      const uint32_t prev = __hip_atomic_fetch_add(&p.counters[c], weight, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      if (prev + weight == 2u * static_cast<uint32_t>(p.tiles_per_chunk)) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
+}
+
+// One workgroup per work unit. With 256-row tiles, a last dispatch round
+// that would leave more than half of the CUs idle is run as half tiles
+// instead (units n_full.. map to the two row halves of tiles n_full..): the
+// round then ends after a 128-row tile's time. Each half still sums all of K
+// once, so results do not depend on the split.
+template <Elem E, bool BT, class TS, Out O>
+__global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
+  constexpr int kSmem = chunked_smem<TS, OutInfo<O>::bytes>();
+  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
+  lds_t* smem = (lds_t*)smem_raw;
+  const int u = xcd_tile(blockIdx.x, p.round, gridDim.x);
+  if constexpr (TS::BM == 256) {
+    using TH = Tile<128, TS::BN, TS::WM, TS::WN>;
+    if (u >= p.n_full) {
+      const int v = u - p.n_full;
+      chunked_tile<E, BT, TH, O>(p, smem, p.n_full + (v >> 1), v & 1, 1u);
+      return;
+    }
+  }
+  chunked_tile<E, BT, TS, O>(p, smem, u, 0, 2u);
 }
 
 // ---------------------------------------------------------------- grouped GEMM
@@ -391,15 +414,24 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   }
 }
 
-// Tile height for a problem: 256-row tiles unless they leave too much of the
-// GPU idle in the last round of tiles, then 128-row tiles (measured on the
-// 8192 x 3072 x 3072 share: 256-row tiles at 75% occupancy of their two
-// rounds still beat 128-row tiles at 100% of three).
+// Tile height for a problem, from the dispatch rounds each choice needs
+// (one workgroup per CU at a time). A 128-row tile costs about 3/4 of a
+// 256-row one (measured on the 8192 x 3072 x 3072 share), so costs are
+// counted in quarter rounds of 256-row tiles; a last 256-row round that is
+// at most half full runs as half tiles (3/4 of a round).
+static bool half_tail(int64_t tiles, int64_t cus) {
+  const int64_t rem = tiles % cus;
+  return rem > 0 && tiles > rem && 2 * rem <= cus;
+}
+
 static bool use_tall_tiles(int64_t mc, int64_t n, int W) {
   const int64_t cus = num_cus();
-  const int64_t tiles = ((mc + 255) / 256) * ((n + 255) / 256) * W;
-  const int64_t rounds = (tiles + cus - 1) / cus;
-  return tiles * 10 >= rounds * cus * 7;  // >= 70% of the slots busy
+  const int64_t tn = (n + 255) / 256;
+  const int64_t tl = ((mc + 255) / 256) * tn * W;
+  const int64_t tm = ((mc + 127) / 128) * tn * W;
+  const int64_t rl = (tl + cus - 1) / cus, rm = (tm + cus - 1) / cus;
+  const int64_t cost_l = half_tail(tl, cus) ? 4 * (rl - 1) + 3 : 4 * rl;
+  return cost_l <= 3 * rm;
 }
 
 static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
@@ -439,8 +471,16 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.flags = flags;
   a.counters = counters;
   a.epoch = epoch;
-  const int64_t blocks = static_cast<int64_t>(a.tiles_per_chunk) * W;
-  if (blocks > 0x7fffffff) return MC2_ERR_SHAPE;
+  const int64_t tiles = static_cast<int64_t>(a.tiles_per_chunk) * W;
+  if (tiles > 0x3fffffff) return MC2_ERR_SHAPE;
+  // A last round filled to at most half runs as half tiles (see the kernel).
+  int64_t blocks = tiles;
+  a.n_full = static_cast<int>(tiles);
+  if (tall && half_tail(tiles, num_cus())) {
+    const int64_t rem = tiles % num_cus();
+    a.n_full = static_cast<int>(tiles - rem);
+    blocks = tiles + rem;
+  }
   hipError_t e;
   if (tall)
     e = x2_trans ? dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)

@@ -141,6 +141,29 @@ def test_rs_flags_reset_between_calls():
         assert counters.cpu().tolist() == [0] * W
 
 
+def test_last_round_as_half_tiles():
+    """More 256-row tiles than CUs, with a last round under half full: those
+    tiles run as two 128-row halves. Chunks of 1000 rows (the last 256-row tile
+    is ragged and its second half partial) and n = 8696 (a ragged column
+    tile); ready flags on, both chunk orders."""
+    W = 2
+    d = wl.gemm_inputs(28, W * 1000, 256, 8696, wl.BF16, std=1.0)
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
+    ref = _oracle_rs(d, W)
+    for rank in (0, 1):
+        out = _run_rs(d, W, rank, flags=(flags, counters), epoch=rank + 5)
+        assert flags.cpu().tolist() == [rank + 5] * W
+        assert counters.cpu().tolist() == [0] * W
+        assert_tol(to_f64(out), ref, f"rs rank {rank}")
+    out = mc2.mc2_ag_mm_local(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 1,
+                              ready_flags=flags, flag_counters=counters, epoch=9)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [9] * W
+    assert counters.cpu().tolist() == [0] * W
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "ag_mm")
+
+
 # ------------------------------------------------------------------ full sizes
 
 def _sample(m, W, n, rng, per_chunk=6, ncols=48):
