@@ -431,7 +431,9 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
 }
 
 // Staged tile -> global with 16-byte coalesced stores; rows >= nrows and bytes
-// >= row_bytes_valid of each destination row are skipped.
+// >= row_bytes_valid of each destination row are skipped. The stores are
+// non-temporal: output is not read again here, and keeping it out of the L2
+// makes the L2 write-back of a ready-flag release short.
 __device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int tile_row_bytes,
                                              int tile_rows, char* out, int64_t ldo, int64_t nrows,
                                              int64_t col_byte0, int64_t row_bytes_valid) {
@@ -440,8 +442,8 @@ __device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int t
   for (int q = threadIdx.x; q < total; q += kThreads) {
     const int r = q / cpr, c = q - r * cpr;
     if (r < nrows && col_byte0 + c * 16 < row_bytes_valid)
-      *reinterpret_cast<u32x4_t*>(out + r * ldo + col_byte0 + c * 16) =
-          *reinterpret_cast<const MC2_LDS u32x4_t*>(smem + r * pitch + c * 16);
+      __builtin_nontemporal_store(*reinterpret_cast<const MC2_LDS u32x4_t*>(smem + r * pitch + c * 16),
+                                  reinterpret_cast<u32x4_t*>(out + r * ldo + col_byte0 + c * 16));
   }
 }
 
