@@ -287,7 +287,7 @@ def main():
         d = wl.c2_inputs()
         done, t0 = 0, time.perf_counter()
         # whole row chunks of the headline workload, repeated until ~10 s of work
-        while time.perf_counter() - t0 < 10.0 and done < 64:
+        while time.perf_counter() - t0 < 10.0 and done < 1024:
             c = done % 8
             og.ag_mm(d["x1"], d["x2"], world_size=8, in_dtype="bf16",
                      rows=np.arange(c * 1024, (c + 1) * 1024))
