@@ -198,7 +198,8 @@ __global__ __launch_bounds__(kMoeThreads) void permute_scatter_kernel(
 
   // Row copy: wave w takes tokens w, w+4, ... of the block; each token row is
   // read once (16-byte chunks, 4 per lane per pass) and stored to its K
-  // destination rows.
+  // destination rows. The permuted buffer is written once and not read here:
+  // non-temporal stores keep it from displacing the rows still to be read.
   const int64_t t0 = (int64_t)b * TB;
   int ntok = TB;
   if (t0 + ntok > T) ntok = (int)(T - t0);
@@ -219,7 +220,8 @@ __global__ __launch_bounds__(kMoeThreads) void permute_scatter_kernel(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int64_t j = base + c * 64 + lane;
-          if (j < CR) dst[j] = v[c];
+          if (j < CR)
+            __builtin_nontemporal_store(bit_cast<u32x4_t>(v[c]), reinterpret_cast<u32x4_t*>(dst) + j);
         }
       }
     }
@@ -230,6 +232,8 @@ __global__ __launch_bounds__(kMoeThreads) void permute_scatter_kernel(
 
 // One wave per token; lanes own 16-byte column chunks (8 bf16). Rows of up to
 // 8 slots are loaded before they are accumulated so that their loads overlap.
+// Every y row is read once and every output row written once: both go
+// non-temporal.
 __global__ __launch_bounds__(kMoeThreads) void unpermute_kernel(
     const uint16_t* __restrict__ y, int64_t y_rows, const int32_t* __restrict__ idx,
     const float* __restrict__ probs, int64_t T, int K, int64_t H, uint16_t* __restrict__ out,
@@ -262,7 +266,8 @@ __global__ __launch_bounds__(kMoeThreads) void unpermute_kernel(
         for (int c = 0; c < 2; ++c) {
           const int64_t j = base + c * 64 + lane;
           v[kk][c] = (p >= 0 && j < CR)
-                         ? reinterpret_cast<const uint4*>(y + (int64_t)p * H)[j]
+                         ? bit_cast<uint4>(__builtin_nontemporal_load(
+                               reinterpret_cast<const u32x4_t*>(y + (int64_t)p * H) + j))
                          : zero4();
         }
         if (p < 0) w[kk] = 0.f;
@@ -289,7 +294,7 @@ __global__ __launch_bounds__(kMoeThreads) void unpermute_kernel(
         o.y = f32_to_bf16_bits(acc[c][2]) | ((uint32_t)f32_to_bf16_bits(acc[c][3]) << 16);
         o.z = f32_to_bf16_bits(acc[c][4]) | ((uint32_t)f32_to_bf16_bits(acc[c][5]) << 16);
         o.w = f32_to_bf16_bits(acc[c][6]) | ((uint32_t)f32_to_bf16_bits(acc[c][7]) << 16);
-        reinterpret_cast<uint4*>(out + t * H)[j] = o;
+        __builtin_nontemporal_store(bit_cast<u32x4_t>(o), reinterpret_cast<u32x4_t*>(out + t * H) + j);
       }
     }
   }
