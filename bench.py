@@ -161,6 +161,17 @@ def main():
         headline = {"ms": ms, "tflops": tf, "wall_s": wall, "flop": flop}
         rows["c2_ag_mm_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
         log(f"C2 AG-MM bf16: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s  ({100 * tf / PEAK_BF16:.1f}% of peak)")
+        # The same launch with consumer-side input flags (all already raised):
+        # the cost of the per-tile wait and its system-scope acquire.
+        inf = torch.full((W,), 1, dtype=torch.int32, device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+        ms_w = timed(lambda: mc2.mc2_ag_mm_local_inflags(
+            x, w, W, 0, inf, 1, out=out, ready_flags=flags, flag_counters=cnt, epoch=1,
+            dev_err=err), 200, 20)
+        assert err.item() == 0
+        rows["c2_ag_mm_bf16_inflags"] = {"ms": ms_w, "TFLOP/s": flop / ms_w / 1e9,
+                                         "frac_peak": flop / ms_w / 1e9 / PEAK_BF16}
+        log(f"C2 with input flags: {ms_w * 1e3:.1f} us  {flop / ms_w / 1e9:.1f} TFLOP/s")
         del x, w, out
 
     # ---------------------------------------------------------------- C3

@@ -124,7 +124,32 @@ struct ChunkedArgs {
   uint32_t* flags;
   uint32_t* counters;
   uint32_t epoch;
+  const uint32_t* in_flags;  // NULL: inputs are present; else wait for in_flags[c]
+  uint32_t in_epoch;
+  uint32_t spin_limit;
+  int32_t* dev_err;
+  int own_chunk;             // the chunk that needs no input flag
 };
+
+// Waits (one thread polls) until input chunk c is marked ready, then acquires
+// at system scope: the producer is another agent. Bounded: after spin_limit
+// polls the tile records MC2_DEVERR_TIMEOUT and goes on.
+__device__ __forceinline__ void wait_input_chunk(const ChunkedArgs& p, int c) {
+  if (threadIdx.x == 0) {
+    bool ready = false;
+    for (uint32_t i = 0; i < p.spin_limit; ++i) {
+      if (__hip_atomic_load(p.in_flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+          p.in_epoch) {
+        ready = true;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ready) atomic_or_err(p.dev_err, MC2_DEVERR_TIMEOUT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "");
+  }
+  __syncthreads();
+}
 
 // Tile column -> global column of B, clamped to the last 16-byte column block.
 struct PlainCols {
@@ -175,6 +200,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
   const int64_t row_end = c * p.mc + p.mc;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
 
+  if (p.in_flags && c != p.own_chunk) wait_input_chunk(p, c);
   typename Mma<E>::acc_t acc[TS::FM][TS::FN];
   BDesc bd{p.B, p.ldb, p.n};
   PlainCols cm{col0, p.n - 16 / ElemInfo<E>::bytes};
@@ -434,10 +460,19 @@ static bool use_tall_tiles(int64_t mc, int64_t n, int W) {
   return cost_l <= 3 * rm;
 }
 
+// Waiting for input chunks (AllGatherMatmul consumer side); none by default.
+struct InputWait {
+  const uint32_t* flags = nullptr;
+  uint32_t epoch = 0;
+  uint32_t spin_limit = 0;
+  int32_t* dev_err = nullptr;
+};
+
 static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
                        int first_chunk, int nsim, int x2_trans, int in_dtype, const void* bias,
                        const float* s1, const float* s2, int out_dtype, void* out,
-                       uint32_t* flags, uint32_t* counters, uint32_t epoch, hipStream_t stream) {
+                       uint32_t* flags, uint32_t* counters, uint32_t epoch, hipStream_t stream,
+                       const InputWait& inw = InputWait{}) {
   const int es = in_dtype == MC2_I8 ? 1 : 2;
   const int os = (out_dtype == MC2_F32 || out_dtype == MC2_I32) ? 4 : 2;
   ChunkedArgs a{};
@@ -471,6 +506,11 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.flags = flags;
   a.counters = counters;
   a.epoch = epoch;
+  a.in_flags = inw.flags;
+  a.in_epoch = inw.epoch;
+  a.spin_limit = inw.spin_limit;
+  a.dev_err = inw.dev_err;
+  a.own_chunk = first_chunk;
   const int64_t tiles = static_cast<int64_t>(a.tiles_per_chunk) * W;
   if (tiles > 0x3fffffff) return MC2_ERR_SHAPE;
   // A last round filled to at most half runs as half tiles (see the kernel).
@@ -538,6 +578,43 @@ extern "C" int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_
   const int first = (rank + 1) % world_size;
   return run_chunked(x1, x2, m, k, n, world_size, first, nsim, x2_trans, in_dtype, bias, x1_scale,
                      x2_scale, out_dtype, out, ready_flags, flag_counters, epoch, stream);
+}
+
+static int check_ag(const void* x_gathered, const void* x2, int64_t m_c, int64_t k, int64_t n,
+                    int world_size, int rank, int x2_trans, int in_dtype, void* out,
+                    uint32_t* ready_flags, uint32_t* flag_counters, uint32_t epoch) {
+  if (!x_gathered || !x2 || !out) return MC2_ERR_NULL;
+  if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
+  if (m_c <= 0 || n <= 0 || k <= 0) return MC2_ERR_SHAPE;
+  if (in_dtype != MC2_F16 && in_dtype != MC2_BF16) return MC2_ERR_DTYPE;
+  if (k % 8 || n % 8) return MC2_ERR_ALIGN;
+  if (!aligned16(x_gathered) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
+  if (!offsets_fit(k * 2, (x2_trans ? k : n) * 2)) return MC2_ERR_UNSUPPORTED;
+  if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
+  if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+  return MC2_OK;
+}
+
+extern "C" int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, int64_t m_c,
+                                       int64_t k, int64_t n, int world_size, int rank,
+                                       int x2_trans, int in_dtype, const void* bias, void* out,
+                                       uint32_t* ready_flags, uint32_t* flag_counters,
+                                       uint32_t epoch, const uint32_t* in_flags,
+                                       uint32_t in_epoch, uint32_t spin_limit, int32_t* dev_err,
+                                       hipStream_t stream) {
+  const int st = check_ag(x_gathered, x2, m_c, k, n, world_size, rank, x2_trans, in_dtype, out,
+                          ready_flags, flag_counters, epoch);
+  if (st) return st;
+  if (!in_flags) return MC2_ERR_NULL;
+  if (in_epoch == 0 || spin_limit == 0) return MC2_ERR_SHAPE;
+  InputWait w;
+  w.flags = in_flags;
+  w.epoch = in_epoch;
+  w.spin_limit = spin_limit;
+  w.dev_err = dev_err;
+  return run_chunked(x_gathered, x2, m_c * world_size, k, n, world_size, rank, 1, x2_trans,
+                     in_dtype, bias, nullptr, nullptr, in_dtype, out, ready_flags, flag_counters,
+                     epoch, stream, w);
 }
 
 extern "C" int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,

@@ -14,7 +14,7 @@ from . import _lib
 
 MC2_F16, MC2_BF16, MC2_I8, MC2_F32, MC2_I32 = 0, 1, 2, 3, 4
 MC2_ACT_NONE, MC2_ACT_SWIGLU = 0, 1
-MC2_DEVERR_EXPERT_ID, MC2_DEVERR_COUNTS, MC2_DEVERR_INDEX = 1, 2, 4
+MC2_DEVERR_EXPERT_ID, MC2_DEVERR_COUNTS, MC2_DEVERR_INDEX, MC2_DEVERR_TIMEOUT = 1, 2, 4, 8
 
 _CODES = {torch.float16: MC2_F16, torch.bfloat16: MC2_BF16, torch.int8: MC2_I8,
           torch.float32: MC2_F32, torch.int32: MC2_I32}
@@ -101,6 +101,32 @@ def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=No
         int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
         _ptr(ready_flags), _ptr(flag_counters), epoch, _stream(dev))
     _check("mc2_ag_mm_local", st)
+    return out
+
+
+def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch, *,
+                            spin_limit=1 << 24, x2_trans=False, bias=None, out=None,
+                            ready_flags=None, flag_counters=None, epoch=0, dev_err=None):
+    """mc2_ag_mm_local whose tiles wait until in_flags[c] == in_epoch before
+    reading gathered chunk c (c != rank). in_flags: W int32 on the GPU or in
+    host-pinned memory."""
+    if in_flags.dtype not in (torch.int32, torch.uint32) or in_flags.numel() != world_size:
+        raise ValueError("in_flags must hold world_size int32")
+    if not in_flags.is_cuda and not in_flags.is_pinned():
+        raise ValueError("in_flags must be GPU or host-pinned memory")
+    dev = _dev(x_gathered, x2, bias, out, ready_flags, flag_counters, dev_err)
+    M, k = x_gathered.shape
+    if M % world_size:
+        raise ValueError("rows of x_gathered must be world_size * m_c")
+    n = x2.shape[0] if x2_trans else x2.shape[1]
+    if out is None:
+        out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
+    st = _lib.load().mc2_ag_mm_local_inflags(
+        x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
+        int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
+        _ptr(ready_flags), _ptr(flag_counters), epoch, in_flags.data_ptr(), in_epoch,
+        spin_limit, _ptr(dev_err), _stream(dev))
+    _check("mc2_ag_mm_local_inflags", st)
     return out
 
 

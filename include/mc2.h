@@ -65,6 +65,8 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
 #define MC2_DEVERR_COUNTS 2u    /* recv_counts disagree with send_counts, or   */
                                 /* the counted rows exceed a buffer's rows     */
 #define MC2_DEVERR_INDEX 4u     /* an unpermute index outside the y buffer     */
+#define MC2_DEVERR_TIMEOUT 8u   /* an input ready flag did not arrive within
+                                   the spin limit                             */
 
 /*
  * mc2_mm_rs_local -- MatmulReduceScatter compute share [RS].
@@ -128,6 +130,36 @@ int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t
                     int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
                     const void* bias, void* out, uint32_t* ready_flags,
                     uint32_t* flag_counters, uint32_t epoch, hipStream_t stream);
+
+/*
+ * mc2_ag_mm_local_inflags -- mc2_ag_mm_local whose tiles wait for their input
+ * chunk: the consumer side of the AllGatherMatmul pipeline [AG, CANN hccl
+ * issue 158; MC2 "执行路径": communication and computation of different chunks
+ * overlap]. Before a tile reads gathered chunk c (c != rank: the own chunk is
+ * local), one thread polls in_flags[c] until it equals in_epoch, then takes
+ * a system-scope acquire fence, so every byte written to chunk c before the
+ * producer's release of in_flags[c] is visible.
+ *
+ *   in_flags   W uint32 in memory the GPU can read (device, or host-pinned);
+ *              written by an agent that does not need this kernel to make
+ *              progress (a copy engine, a peer, the host): the kernel never
+ *              raises them itself, so it cannot deadlock on them.
+ *   in_epoch   value that marks chunk c ready (nonzero).
+ *   spin_limit polls before a tile gives up (>= 1; a poll sleeps ~64 clocks).
+ *              A tile that gives up ORs MC2_DEVERR_TIMEOUT into *dev_err and
+ *              computes on the data it finds, so the call always completes and
+ *              the ready-flag counters stay consistent; its output is then
+ *              undefined.
+ *   dev_err    NULL or one int32.
+ * Other arguments, results and errors as mc2_ag_mm_local; in_flags NULL is
+ * MC2_ERR_NULL, in_epoch == 0 or spin_limit == 0 is MC2_ERR_SHAPE.
+ */
+int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
+                            int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
+                            const void* bias, void* out, uint32_t* ready_flags,
+                            uint32_t* flag_counters, uint32_t epoch, const uint32_t* in_flags,
+                            uint32_t in_epoch, uint32_t spin_limit, int32_t* dev_err,
+                            hipStream_t stream);
 
 /*
  * mc2_moe_histc -- token count per expert [EP "执行路径": torch.histc with

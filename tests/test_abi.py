@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -115,3 +115,13 @@ def test_moe_entry_points_reject(lib):
     assert U(FAKE, 10, FAKE, FAKE, 4, 0, 64, FAKE, None, None) == ERR_SHAPE
     assert U(FAKE, 10, FAKE, FAKE, 4, 2, 4, FAKE, None, None) == ERR_SHAPE
     assert U(FAKE, 10, FAKE, FAKE, 4, 2, 68, FAKE, None, None) == ERR_ALIGN
+
+
+def test_ag_mm_inflags_validates(lib):
+    f = lib.mc2_ag_mm_local_inflags
+    base = (FAKE, FAKE, 100, 512, 264, 8, 0, 0, BF16, None, FAKE, None, None, 0)
+    assert f(*base, None, 1, 100, None, None) == ERR_NULL      # in_flags required
+    assert f(*base, FAKE, 0, 100, None, None) == ERR_SHAPE     # in_epoch != 0
+    assert f(*base, FAKE, 1, 0, None, None) == ERR_SHAPE       # spin_limit >= 1
+    assert f(None, *base[1:], FAKE, 1, 100, None, None) == ERR_NULL
+    assert f(*base[:8], I8, *base[9:], FAKE, 1, 100, None, None) == ERR_DTYPE

@@ -164,6 +164,87 @@ def test_last_round_as_half_tiles():
     assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "ag_mm")
 
 
+# ------------------------------------------------- AllGatherMatmul input flags
+
+def _hip():
+    """The HIP runtime this process already uses (the one torch loaded)."""
+    import ctypes as C
+    path = next(line.split()[-1] for line in open("/proc/self/maps")
+                if "libamdhip64.so" in line)
+    lib = C.CDLL(path)
+    lib.hipStreamWriteValue32.restype = C.c_int
+    lib.hipStreamWriteValue32.argtypes = [C.c_void_p, C.c_void_p, C.c_uint32, C.c_uint]
+    return lib
+
+
+def test_ag_mm_inflags_all_present():
+    W = 4
+    d = wl.gemm_inputs(41, W * 130, 512, 264, wl.BF16, std=1.0)
+    inf = torch.full((W,), 77, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(W, dtype=torch.int32, device="cuda")
+    out = mc2.mc2_ag_mm_local_inflags(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 2,
+                                      inf, 77, ready_flags=flags, flag_counters=cnt, epoch=3,
+                                      dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert flags.cpu().tolist() == [3] * W and cnt.cpu().tolist() == [0] * W
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "inflags")
+
+
+def test_ag_mm_inflags_raised_later_by_another_agent():
+    """The input flags of the three remote chunks are raised one by one, 3 ms
+    apart and in reverse order, by stream writes (executed by the command
+    processor, not by this kernel) while the kernel runs: the kernel's tiles
+    wait for them, and the result is exact."""
+    import time
+    W, rank = 4, 1
+    d = wl.gemm_inputs(42, W * 130, 512, 264, wl.BF16, std=1.0)
+    x, w = to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16")
+    inf = torch.zeros(W, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    hip = _hip()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    out = mc2.mc2_ag_mm_local_inflags(x, w, W, rank, inf, 5, spin_limit=200000, dev_err=err)
+    t1.record()
+    for c in (0, 3, 2):  # remote chunks, reverse of the compute order 2, 3, 0
+        time.sleep(0.003)
+        assert hip.hipStreamWriteValue32(side.cuda_stream, inf.data_ptr() + 4 * c, 5, 0) == 0
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert t0.elapsed_time(t1) > 6.0, "the kernel did not wait for the flags"
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "late flags")
+
+
+def test_ag_mm_inflags_timeout_reported_and_state_kept():
+    """A flag that never arrives: with a small spin limit every tile of that
+    chunk gives up, MC2_DEVERR_TIMEOUT is set, the kernel ends normally, and
+    the ready-flag counters are left consistent for the next call."""
+    W = 4
+    d = wl.gemm_inputs(43, W * 130, 512, 264, wl.BF16, std=1.0)
+    x, w = to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16")
+    inf = torch.tensor([9, 9, 0, 9], dtype=torch.int32, device="cuda")  # chunk 2 never ready
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(W, dtype=torch.int32, device="cuda")
+    mc2.mc2_ag_mm_local_inflags(x, w, W, 0, inf, 9, spin_limit=64, ready_flags=flags,
+                                flag_counters=cnt, epoch=1, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == mc2.MC2_DEVERR_TIMEOUT
+    assert cnt.cpu().tolist() == [0] * W and flags.cpu().tolist() == [1] * W
+    inf[2] = 9
+    err.zero_()
+    out = mc2.mc2_ag_mm_local_inflags(x, w, W, 0, inf, 9, spin_limit=64, ready_flags=flags,
+                                      flag_counters=cnt, epoch=2, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0 and flags.cpu().tolist() == [2] * W
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "after")
+
+
 # ------------------------------------------------------------------ full sizes
 
 def _sample(m, W, n, rng, per_chunk=6, ncols=48):
