@@ -16,6 +16,11 @@ Sources (page title, section):
   the basic case and ``output_dtype`` in the quantized case.
 * CANN hccl issue 158: ``npu_all_gather_base_mm(x1, x2, hcom, world_size)``
   computes ``allgather(x1) @ x2``.
+* "NPU Training Operators - MC2", "底层 API 对照" and the MindSpeed-LLM
+  description it quotes: ``npu_mm_all_reduce_base`` fuses the TP matmul with
+  all_reduce, every rank ending with the sum of the W partials; same page,
+  "风险": MC2 may cost precision on some models. The mc2_all_reduce article
+  ("先搞懂AllReduce为什么慢"): ``full_out = all_reduce(x @ weights_shard)``.
 
 Arithmetic is float64; the int8 products are integers whose partial sums stay
 below 2**53 for every k the API accepts (k < 65535, |value| <= 127), so the
@@ -150,3 +155,57 @@ def ag_mm(x_gathered, x2, *, world_size, in_dtype, x2_trans=False, bias=None,
         bv = decode(bias, in_dtype)
         P = P + (bv[cols] if cols is not None else bv)[None, :]
     return round_to(P, in_dtype)
+
+
+AR_ONE_ROUNDING, AR_RANK_ROUNDED, AR_HOP_ROUNDED = 0, 1, 2
+
+
+def ar_sum(partials, *, dtype, rounding):
+    """The all-reduce sum of W partials already in ``dtype`` storage, (W, ...)
+    -> (...), rounded to ``dtype``.
+
+    * AR_RANK_ROUNDED: the W stored partials summed exactly (float64, rank
+      order) and rounded once;
+    * AR_HOP_ROUNDED: a running sum rounded to ``dtype`` after every addition,
+      in rank order: s = p_0, s = round(s + p_w) for w = 1 .. W-1 (a ring
+      reduction carried out in the storage dtype).
+    """
+    P = decode(np.asarray(partials), dtype)
+    if rounding == AR_RANK_ROUNDED:
+        s = np.zeros(P.shape[1:])
+        for w in range(P.shape[0]):
+            s = s + P[w]
+        return round_to(s, dtype)
+    if rounding == AR_HOP_ROUNDED:
+        s = P[0].copy()
+        for w in range(1, P.shape[0]):
+            s = round_to(s + P[w], dtype)
+        return s
+    raise ValueError(rounding)
+
+
+def mm_ar(x1, x2, *, world_size, in_dtype, x2_trans=False, bias=None, rounding=AR_ONE_ROUNDING,
+          rows=None, cols=None):
+    """MatmulAllReduce local share: every rank ends with the full (m, n)
+    ``P = sum_w (x1_w @ x2_w + bias)`` of the W partials, x1 (W, m, k) and x2
+    (W, k, n) (or (W, n, k) with ``x2_trans``) stacked as in ``mm_rs``.
+
+    * AR_ONE_ROUNDING: the sum rounded once (one accumulator over all W
+      partials, as the fused kernel keeps it);
+    * AR_RANK_ROUNDED / AR_HOP_ROUNDED: each rank's partial is first rounded to
+      ``in_dtype`` (what a rank sends), then combined by ``ar_sum``.
+    """
+    # every rank keeps all rows: no row chunking (world_size only counts partials)
+    if rounding == AR_ONE_ROUNDING:
+        return mm_rs(x1, x2, world_size=1, in_dtype=in_dtype, nsim=world_size,
+                     x2_trans=x2_trans, bias=bias, rows=rows, cols=cols)
+    parts = [mm_rs(np.asarray(x1)[w], np.asarray(x2)[w], world_size=1, in_dtype=in_dtype,
+                   x2_trans=x2_trans, bias=bias, rows=rows, cols=cols)
+             for w in range(world_size)]
+    # round_to returns float64 values on the dtype's grid; ar_sum reads storage
+    stored = np.stack(parts)
+    if in_dtype == "bf16":
+        stored = (stored.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        stored = stored.astype(np.float16)
+    return ar_sum(stored, dtype=in_dtype, rounding=rounding)

@@ -418,3 +418,64 @@ def test_per_token_outputs_match_the_chain():
     h, y = moe.expert_ffn_rows(d["x"][slots // 3], d["sel"].reshape(-1)[slots] - 4, d["w1"], d["w2"])
     np.testing.assert_array_equal(h, r["h"])
     np.testing.assert_array_equal(y, r["y_full"][start:start + n])
+
+
+# ---------------------------------------------------------------- MatmulAllReduce
+
+def _bf(vals):
+    return (np.asarray(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_mm_ar_rounding_modes_hand_worked_bf16():
+    """bf16 spacing at 1 is 2**-7. Rank 0's partial 1 + 2**-8 sits exactly half
+    way between 1 and 1 + 2**-7 and rounds (ties to even) to 1; rank 1's partial
+    2**-8 is exact. The exact sum 1 + 2**-7 is a bf16 value: one rounding keeps
+    it, rounding each rank's partial first loses it."""
+    x1 = np.stack([_bf([[1.0, 2.0 ** -8]]), _bf([[2.0 ** -8, 0.0]])])
+    x2 = np.stack([_bf([[1.0], [1.0]])] * 2)
+    got = [gemm.mm_ar(x1, x2, world_size=2, in_dtype="bf16", rounding=r)[0, 0] for r in range(3)]
+    assert got == [1.0 + 2.0 ** -7, 1.0, 1.0]
+
+
+def test_mm_ar_hop_rounding_differs_from_rank_rounding():
+    """Partials 1, 2**-8, 2**-8 are all bf16 values. Summed exactly they give
+    1 + 2**-7 (a bf16 value); a running sum rounded after each addition stays
+    at 1 (1 + 2**-8 is a tie that rounds to even twice)."""
+    x1 = np.stack([_bf([[1.0]]), _bf([[2.0 ** -8]]), _bf([[2.0 ** -8]])])
+    x2 = np.stack([_bf([[1.0]])] * 3)
+    got = [gemm.mm_ar(x1, x2, world_size=3, in_dtype="bf16", rounding=r)[0, 0] for r in range(3)]
+    assert got == [1.0 + 2.0 ** -7, 1.0 + 2.0 ** -7, 1.0]
+
+
+def test_mm_ar_rounding_modes_hand_worked_f16():
+    """fp16 spacing at 1 is 2**-10: the same tie one binade of precision down."""
+    x1 = np.stack([np.array([[1.0, 2.0 ** -11]], np.float16),
+                   np.array([[2.0 ** -11, 0.0]], np.float16)])
+    x2 = np.stack([np.ones((2, 1), np.float16)] * 2)
+    got = [gemm.mm_ar(x1, x2, world_size=2, in_dtype="f16", rounding=r)[0, 0] for r in range(3)]
+    assert got == [1.0 + 2.0 ** -10, 1.0, 1.0]
+
+
+def test_ar_sum_small_integers_exact_and_w1_identity():
+    parts = _bf([[3.0, -7.0], [5.0, 2.0], [-2.0, 4.0]])
+    for r in (gemm.AR_RANK_ROUNDED, gemm.AR_HOP_ROUNDED):
+        np.testing.assert_array_equal(gemm.ar_sum(parts, dtype="bf16", rounding=r), [6.0, -1.0])
+    rng = np.random.default_rng(5)
+    one = _bf(rng.standard_normal((1, 64)).astype(np.float32))
+    for r in (gemm.AR_RANK_ROUNDED, gemm.AR_HOP_ROUNDED):
+        np.testing.assert_array_equal(gemm.ar_sum(one, dtype="bf16", rounding=r),
+                                      numerics.decode(one[0], "bf16"))
+
+
+def test_mm_ar_precision_risk_grows_with_roundings():
+    """The precision risk of rounding partials before the all-reduce: on N(0,1)
+    data with W = 8 the mean error against the exact sum grows from one
+    rounding to per-rank rounding to per-hop rounding."""
+    rng = np.random.default_rng(6)
+    W, m, k, n = 8, 32, 64, 48
+    x1 = _bf(rng.standard_normal((W, m, k)).astype(np.float32))
+    x2 = _bf(rng.standard_normal((W, k, n)).astype(np.float32))
+    exact = sum(numerics.decode(x1[w], "bf16") @ numerics.decode(x2[w], "bf16") for w in range(W))
+    err = [np.mean(np.abs(gemm.mm_ar(x1, x2, world_size=W, in_dtype="bf16", rounding=r) - exact))
+           for r in range(3)]
+    assert err[0] < err[1] < err[2]
