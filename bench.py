@@ -283,7 +283,26 @@ def main():
             tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
             rows["c5b_sim_rs_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
             log(f"C5b sim-W=8 MM-RS: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
-            del x1, x2, out
+            # MatmulAllReduce local share on the same partials, per rounding model
+            ws = torch.empty(mc2.mc2_mm_ar_workspace_size(16384, 8192, W, torch.bfloat16,
+                                                          mc2.MC2_AR_HOP_ROUNDED),
+                             dtype=torch.uint8, device=dev)
+            for mode, name in ((mc2.MC2_AR_ONE_ROUNDING, "one"), (mc2.MC2_AR_RANK_ROUNDED, "rank"),
+                               (mc2.MC2_AR_HOP_ROUNDED, "hop")):
+                ms = timed(lambda: mc2.mc2_mm_ar_local(x1, x2, W, rounding=mode, out=out,
+                                                       workspace=ws), 30, 3)
+                tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
+                rows[f"c5b_mm_ar_{name}_rounding_bf16"] = {"ms": ms, "TFLOP/s": tf,
+                                                           "frac_peak": tf / PEAK_BF16}
+                log(f"C5b MM-AR ({name} rounding): {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
+            # the combining step alone: W stored partials read, one result written
+            parts = ws[: W * 16384 * 8192 * 2].view(torch.bfloat16).view(W, 16384, 8192)
+            ms = timed(lambda: mc2.mc2_ar_sum_local(parts, mc2.MC2_AR_HOP_ROUNDED, out=out), 50, 5)
+            nbytes = (W + 1) * 16384 * 8192 * 2
+            rows["c5b_ar_sum_bf16"] = {"ms": ms, "GB/s": nbytes / ms / 1e6,
+                                       "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM}
+            log(f"C5b AR combine: {ms * 1e3:.1f} us  {nbytes / ms / 1e6:.0f} GB/s")
+            del x1, x2, out, ws, parts
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None

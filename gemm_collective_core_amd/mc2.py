@@ -14,6 +14,7 @@ from . import _lib
 
 MC2_F16, MC2_BF16, MC2_I8, MC2_F32, MC2_I32 = 0, 1, 2, 3, 4
 MC2_ACT_NONE, MC2_ACT_SWIGLU = 0, 1
+MC2_AR_ONE_ROUNDING, MC2_AR_RANK_ROUNDED, MC2_AR_HOP_ROUNDED = 0, 1, 2
 MC2_DEVERR_EXPERT_ID, MC2_DEVERR_COUNTS, MC2_DEVERR_INDEX, MC2_DEVERR_TIMEOUT = 1, 2, 4, 8
 
 _CODES = {torch.float16: MC2_F16, torch.bfloat16: MC2_BF16, torch.int8: MC2_I8,
@@ -127,6 +128,49 @@ def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch
         _ptr(ready_flags), _ptr(flag_counters), epoch, in_flags.data_ptr(), in_epoch,
         spin_limit, _ptr(dev_err), _stream(dev))
     _check("mc2_ag_mm_local_inflags", st)
+    return out
+
+
+def mc2_mm_ar_workspace_size(m, n, world_size, in_dtype, rounding) -> int:
+    code = _CODES[in_dtype] if isinstance(in_dtype, torch.dtype) else int(in_dtype)
+    return int(_lib.load().mc2_mm_ar_workspace_size(m, n, world_size, code, rounding))
+
+
+def mc2_mm_ar_local(x1, x2, world_size, *, rounding=MC2_AR_ONE_ROUNDING, x2_trans=False,
+                    bias=None, out=None, workspace=None):
+    """MatmulAllReduce local share: the full (m, n) sum of the W stacked
+    partials x1 (W, m, k) @ x2 (W, k, n) (or (W, n, k) with x2_trans), combined
+    under `rounding`. A workspace is allocated when the mode needs one and
+    none is given."""
+    dev = _dev(x1, x2, bias, out, workspace)
+    if x1.dim() != 3 or x2.dim() != 3 or x1.shape[0] != world_size or x2.shape[0] != world_size:
+        raise ValueError("x1 and x2 must be stacked (world_size, ., .)")
+    _, m, k = x1.shape
+    n = x2.shape[1] if x2_trans else x2.shape[2]
+    if (x2.shape[2] if x2_trans else x2.shape[1]) != k:
+        raise ValueError("k mismatch between x1 and x2")
+    if out is None:
+        out = torch.empty((m, n), dtype=x1.dtype, device=dev)
+    need = mc2_mm_ar_workspace_size(m, n, world_size, x1.dtype, rounding)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib.load().mc2_mm_ar_local(
+        x1.data_ptr(), x2.data_ptr(), m, k, n, world_size, int(bool(x2_trans)), _CODES[x1.dtype],
+        _ptr(bias), rounding, out.data_ptr(), _ptr(workspace), ws_bytes, _stream(dev))
+    _check("mc2_mm_ar_local", st)
+    return out
+
+
+def mc2_ar_sum_local(partials, rounding, *, out=None):
+    """The all-reduce combining step: partials (W, ...) -> out (...)."""
+    dev = _dev(partials, out)
+    W = partials.shape[0]
+    if out is None:
+        out = torch.empty(partials.shape[1:], dtype=partials.dtype, device=dev)
+    st = _lib.load().mc2_ar_sum_local(partials.data_ptr(), W, out.numel(), _CODES[partials.dtype],
+                                      rounding, out.data_ptr(), _stream(dev))
+    _check("mc2_ar_sum_local", st)
     return out
 
 

@@ -162,6 +162,49 @@ int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, int64_t m_c,
                             hipStream_t stream);
 
 /*
+ * MatmulAllReduce local share ["NPU Training Operators - MC2", "底层 API 对照":
+ * npu_mm_all_reduce_base fuses the TP matmul with all_reduce; same page,
+ * "风险": MC2 may cost precision]. Every rank ends with the full
+ *
+ *   P = sum_{w < W} (x1_w @ x2_w + bias)        x1 (W, m, k), x2 (W, k, n) or
+ *                                               (W, n, k) with x2_trans
+ *
+ * (m, n) in in_dtype (MC2_F16 or MC2_BF16); no row chunking, so m need not be
+ * divisible by W. rounding selects how the W partials are combined:
+ *   MC2_AR_ONE_ROUNDING  one fp32 accumulator over all W*k products, rounded
+ *                        once (the fused kernel; no workspace);
+ *   MC2_AR_RANK_ROUNDED  each rank's partial rounded to in_dtype (what a rank
+ *                        sends), the W rounded partials summed exactly in
+ *                        rank order and rounded once;
+ *   MC2_AR_HOP_ROUNDED   as RANK_ROUNDED, but the running sum rounded to in_dtype
+ *                        after every addition (a ring reduction carried out
+ *                        in the storage dtype).
+ * The last two keep the W partials in `workspace` (caller-owned, 16-byte
+ * aligned, >= mc2_mm_ar_workspace_size bytes, no initialisation needed;
+ * NULL is MC2_ERR_NULL, smaller is MC2_ERR_WORKSPACE); once the stream has
+ * run the call, it holds the rounded partials as (W, m, n) in in_dtype. Constraints: W in
+ * {1, 2, 4, 8, 16, 32}; 1 <= k < 65535; k % 8 == 0; n % 8 == 0.
+ *
+ * mc2_ar_sum_local is the combining step alone: out (elems) = the sum of the
+ * W stored partials (W, elems) under MC2_AR_RANK_ROUNDED or
+ * MC2_AR_HOP_ROUNDED, summed in fp64 in rank order and rounded to dtype with
+ * round-to-nearest-even. Constraints: 1 <= W <= 32; elems % 8 == 0;
+ * 16-byte aligned pointers.
+ */
+#define MC2_AR_ONE_ROUNDING 0
+#define MC2_AR_RANK_ROUNDED 1
+#define MC2_AR_HOP_ROUNDED 2
+
+size_t mc2_mm_ar_workspace_size(int64_t m, int64_t n, int world_size, int in_dtype, int rounding);
+
+int mc2_mm_ar_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
+                    int world_size, int x2_trans, int in_dtype, const void* bias, int rounding,
+                    void* out, void* workspace, size_t ws_bytes, hipStream_t stream);
+
+int mc2_ar_sum_local(const void* partials, int world_size, int64_t elems, int dtype,
+                     int rounding, void* out, hipStream_t stream);
+
+/*
  * mc2_moe_histc -- token count per expert [EP "执行路径": torch.histc with
  * bins = num_experts, min = 0, max = num_experts]:
  *   counts[e] = #{ i < n_ids : sel[i] == e },  0 <= e < num_experts.

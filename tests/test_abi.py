@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 11, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -125,3 +125,24 @@ def test_ag_mm_inflags_validates(lib):
     assert f(*base, FAKE, 1, 0, None, None) == ERR_SHAPE       # spin_limit >= 1
     assert f(None, *base[1:], FAKE, 1, 100, None, None) == ERR_NULL
     assert f(*base[:8], I8, *base[9:], FAKE, 1, 100, None, None) == ERR_DTYPE
+
+
+def test_mm_ar_validates(lib):
+    f = lib.mc2_mm_ar_local
+    assert lib.mc2_mm_ar_workspace_size(100, 64, 4, BF16, 0) == 0
+    assert lib.mc2_mm_ar_workspace_size(100, 64, 4, BF16, 1) == 4 * 100 * 64 * 2
+    assert lib.mc2_mm_ar_workspace_size(100, 64, 3, BF16, 1) == 0   # world sizes 1, 2, 4, ...
+    assert lib.mc2_mm_ar_workspace_size(100, 64, 4, I8, 2) == 0
+    base = (FAKE, FAKE, 100, 512, 64, 4, 0, BF16, None)
+    assert f(*base, 1, FAKE, None, 0, None) == ERR_NULL            # the mode needs a workspace
+    assert f(*base, 1, FAKE, FAKE, 16, None) == ERR_WS             # too small
+    assert f(*base, 1, FAKE, FAKE + 8, 1 << 20, None) == ERR_ALIGN
+    assert f(*base, 3, FAKE, None, 0, None) == ERR_SHAPE           # unknown mode
+    assert f(FAKE, FAKE, 100, 512, 64, 3, 0, BF16, None, 0, FAKE, None, 0, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 100, 512, 64, 4, 0, I8, None, 0, FAKE, None, 0, None) == ERR_DTYPE
+    assert f(FAKE, FAKE, 100, 516, 64, 4, 0, BF16, None, 0, FAKE, None, 0, None) == ERR_ALIGN
+    g = lib.mc2_ar_sum_local
+    assert g(FAKE, 4, 1024, BF16, 0, FAKE, None) == ERR_SHAPE       # the sum step needs mode 1 or 2
+    assert g(FAKE, 33, 1024, BF16, 1, FAKE, None) == ERR_SHAPE
+    assert g(FAKE, 4, 1020, BF16, 1, FAKE, None) == ERR_ALIGN
+    assert g(FAKE, 4, 1024, F32, 1, FAKE, None) == ERR_DTYPE
