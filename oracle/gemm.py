@@ -59,6 +59,36 @@ def chunk_order(world_size: int, rank: int, kind: str) -> list[int]:
     raise ValueError(kind)
 
 
+def sub_chunk_rows(m: int, world_size: int, c: int, comm_turn: int, j: int) -> slice:
+    """Rows of piece ``j`` of destination chunk ``c`` when the chunk is split
+    ``comm_turn`` ways ([RS] "参数说明": comm_turn is the split granularity of
+    the exchange between ranks, 0 meaning the default split).
+
+    0 (the default) and 1 keep the chunk whole. s > 1 cuts its m_c rows into s
+    contiguous pieces in row order whose sizes differ by at most one, the
+    longer ones first: q = m_c // s rows each, plus one for the first m_c % s
+    pieces. Every piece must be non-empty, so s <= m_c.
+    """
+    rows = chunk_rows(m, world_size, c)
+    s = max(comm_turn, 1)
+    mc = rows.stop - rows.start
+    if s > mc:
+        raise ValueError("more pieces than rows in a chunk")
+    if not 0 <= j < s:
+        raise ValueError("piece index out of range")
+    q, r = divmod(mc, s)
+    start = rows.start + j * q + min(j, r)
+    return slice(start, start + q + (1 if j < r else 0))
+
+
+def segment_order(world_size: int, rank: int, kind: str, comm_turn: int) -> list[tuple[int, int]]:
+    """Order of the (chunk, piece) segments: the chunks in ``chunk_order``, the
+    pieces of each chunk in row order. Segment (c, j) owns ready flag
+    c * max(comm_turn, 1) + j."""
+    s = max(comm_turn, 1)
+    return [(c, j) for c in chunk_order(world_size, rank, kind) for j in range(s)]
+
+
 def _stack(a, nsim):
     a = np.asarray(a)
     return a[None] if (nsim == 1 and a.ndim == 2) else a

@@ -210,6 +210,43 @@ def test_chunk_rows_requires_divisible_m():
     assert gemm.chunk_rows(128, 2, 1) == slice(64, 128)
 
 
+def test_sub_chunk_rows_hand_worked():
+    # m = 20, W = 2: chunk 1 is rows 10..19; three pieces of 4, 3, 3 rows
+    got = [gemm.sub_chunk_rows(20, 2, 1, 3, j) for j in range(3)]
+    assert got == [slice(10, 14), slice(14, 17), slice(17, 20)]
+    # the default split and a split of one keep the chunk whole
+    assert gemm.sub_chunk_rows(20, 2, 0, 0, 0) == slice(0, 10)
+    assert gemm.sub_chunk_rows(20, 2, 0, 1, 0) == slice(0, 10)
+    # an even split: 4 pieces of 256 rows of a 1024-row chunk
+    assert gemm.sub_chunk_rows(8192, 8, 3, 4, 2) == slice(3 * 1024 + 512, 3 * 1024 + 768)
+
+
+@pytest.mark.parametrize("m,W,s", [(64, 4, 3), (96, 2, 7), (40, 8, 5), (1024, 1, 9)])
+def test_sub_chunks_partition_each_chunk(m, W, s):
+    for c in range(W):
+        pieces = [gemm.sub_chunk_rows(m, W, c, s, j) for j in range(s)]
+        rows = np.concatenate([np.arange(p.start, p.stop) for p in pieces])
+        np.testing.assert_array_equal(rows, np.arange(m)[gemm.chunk_rows(m, W, c)])
+        sizes = [p.stop - p.start for p in pieces]
+        assert max(sizes) - min(sizes) <= 1 and min(sizes) >= 1
+        assert sizes == sorted(sizes, reverse=True)
+
+
+def test_sub_chunk_rows_rejects_empty_pieces():
+    with pytest.raises(ValueError):
+        gemm.sub_chunk_rows(16, 4, 0, 5, 0)
+    with pytest.raises(ValueError):
+        gemm.sub_chunk_rows(16, 4, 0, 2, 2)
+
+
+def test_segment_order():
+    assert gemm.segment_order(2, 1, "rs", 2) == [(0, 0), (0, 1), (1, 0), (1, 1)]
+    assert gemm.segment_order(4, 1, "ag", 0) == [(1, 0), (2, 0), (3, 0), (0, 0)]
+    order = gemm.segment_order(8, 5, "rs", 3)
+    assert sorted(c * 3 + j for c, j in order) == list(range(24))
+    assert order[-3:] == [(5, 0), (5, 1), (5, 2)]
+
+
 # ----------------------------------------------------------------- MoE
 
 def test_histc_against_torch_histc_and_bincount():

@@ -105,3 +105,33 @@ def test_histc_off_by_one_is_caught(monkeypatch):
     real = moe.histc
     monkeypatch.setattr(moe, "histc", lambda sel, E: np.roll(real(sel, E), 1))
     _fails(pins.test_histc_against_torch_histc_and_bincount)
+
+
+def test_longer_pieces_last_is_caught(monkeypatch):
+    real = gemm.sub_chunk_rows
+
+    def longer_last(m, W, c, s, j):
+        # the remainder rows given to the last pieces instead of the first
+        k = max(s, 1)
+        mirrored = real(m, W, c, s, k - 1 - j)
+        rows = gemm.chunk_rows(m, W, c)
+        return slice(rows.start + rows.stop - mirrored.stop, rows.start + rows.stop - mirrored.start)
+    monkeypatch.setattr(gemm, "sub_chunk_rows", longer_last)
+    _fails(pins.test_sub_chunk_rows_hand_worked)
+
+
+def test_piece_start_off_by_one_is_caught(monkeypatch):
+    real = gemm.sub_chunk_rows
+
+    def shifted(m, W, c, s, j):
+        r = real(m, W, c, s, j)
+        return slice(r.start + (1 if j else 0), r.stop)
+    monkeypatch.setattr(gemm, "sub_chunk_rows", shifted)
+    _fails(pins.test_sub_chunks_partition_each_chunk, 64, 4, 3)
+
+
+def test_pieces_before_chunks_is_caught(monkeypatch):
+    def piece_major(W, rank, kind, s):
+        return [(c, j) for j in range(max(s, 1)) for c in gemm.chunk_order(W, rank, kind)]
+    monkeypatch.setattr(gemm, "segment_order", piece_major)
+    _fails(pins.test_segment_order)
