@@ -12,7 +12,7 @@ sample of the headline workload.
 Inputs are seeded synthetic data resident in HBM before timing starts. Times
 come from HIP events on the stream the kernels are launched on.
 
-    python bench.py [--steps K] [--warmup W] [--only c2|c3|c4|c5a|c5b|all]
+    python bench.py [--steps K] [--warmup W] [--only c2|c3|c4|c5a|c5b|split|all]
                     [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
@@ -303,6 +303,66 @@ def main():
                                        "frac_hbm": nbytes / ms / 1e6 / PEAK_HBM}
             log(f"C5b AR combine: {ms * 1e3:.1f} us  {nbytes / ms / 1e6:.0f} GB/s")
             del x1, x2, out, ws, parts
+
+    # ---------------------------------------------------------------- split granularity
+    if only in ("all", "split"):
+        # comm_turn pieces: cost of the finer flags, and when the host sees the
+        # first and the last segment flag (flags in host-pinned memory, polled
+        # from the moment the launch call returns; median of `reps` launches)
+        def flag_times(launch, hf, reps):
+            v = hf.numpy()
+            firsts, lasts = [], []
+            for r in range(reps):
+                torch.cuda.synchronize()
+                e = 1000 + r
+                launch(e)
+                t0 = time.perf_counter()
+                seen = np.full(v.size, np.nan)
+                while np.isnan(seen).any():
+                    now = time.perf_counter()
+                    seen[(v == e) & np.isnan(seen)] = now - t0
+                    if now - t0 > 2.0:
+                        raise RuntimeError("segment flags did not arrive")
+                torch.cuda.synchronize()
+                firsts.append(np.min(seen))
+                lasts.append(np.max(seen))
+            return float(np.median(firsts)) * 1e6, float(np.median(lasts)) * 1e6
+
+        log("split: generating inputs")
+        d = wl.c2_inputs()
+        _, b = wl.c5_inputs()
+        W = 8
+        cases = {
+            "c2_ag_mm": (lambda S, out, fl, cn, e: mc2.mc2_ag_mm_local(
+                xc2, wc2, W, 0, out=out, ready_flags=fl, flag_counters=cn, epoch=e, comm_turn=S),
+                (8192, 3072), 2.0 * 8192 * 3072 * 3072, 200),
+            "c5b_sim_rs": (lambda S, out, fl, cn, e: mc2.mc2_mm_rs_local(
+                x1b, x2b, W, 0, out=out, ready_flags=fl, flag_counters=cn, epoch=e, comm_turn=S),
+                (16384, 8192), 2.0 * 8 * 16384 * 1024 * 8192, 30),
+        }
+        xc2, wc2 = to_dev(d["x1"], True), to_dev(d["x2"], True)
+        x1b, x2b = to_dev(b["x1"], True), to_dev(b["x2"], True)
+        split = {}
+        for name, (call, shape, flop, iters) in cases.items():
+            out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+            for S in (1, 2, 4, 8):
+                fl = torch.zeros(W * S, dtype=torch.int32, device=dev)
+                cn = torch.zeros(W * S, dtype=torch.int32, device=dev)
+                ep = [0]
+
+                def step():
+                    ep[0] += 1
+                    call(S, out, fl, cn, ep[0])
+                ms = timed(step, iters, max(iters // 10, 2))
+                hf = torch.zeros(W * S, dtype=torch.int32, pin_memory=True)
+                first, last = flag_times(lambda e: call(S, out, hf, cn, e), hf, 15)
+                split[f"{name}_comm_turn{S}"] = {
+                    "ms": ms, "TFLOP/s": flop / ms / 1e9, "first_flag_us": first,
+                    "last_flag_us": last}
+                log(f"split {name} comm_turn={S}: {ms * 1e3:.1f} us {flop / ms / 1e9:.1f} TFLOP/s;"
+                    f" host sees first/last flag at {first:.0f}/{last:.0f} us")
+        rows["split"] = split
+        del xc2, wc2, x1b, x2b, out
 
     # ---------------------------------------------------------------- CPU oracle
     cpu = None

@@ -117,28 +117,32 @@ struct ChunkedArgs {
   KSpan ks;
   int64_t mc;             // rows per chunk
   int world, first_chunk;
-  int tiles_m, tiles_n, tiles_per_chunk;
+  // Each chunk is cut into `sub` pieces (segments) of sq rows, plus one row
+  // for the first sr; a long piece has tiles_m1 tile rows, a short one tiles_m0.
+  int sub, sr;
+  int64_t sq;
+  int tiles_m1, tiles_m0, tiles_n, tiles_long, tiles_short, tiles_per_chunk;
   int round;              // workgroups per dispatch round (CUs, multiple of 8); 0: no remap
   int n_full;             // work units below n_full are whole tiles, the rest half tiles
   float bias_mul;
   uint32_t* flags;
   uint32_t* counters;
   uint32_t epoch;
-  const uint32_t* in_flags;  // NULL: inputs are present; else wait for in_flags[c]
+  const uint32_t* in_flags;  // NULL: inputs are present; else wait for in_flags[segment]
   uint32_t in_epoch;
   uint32_t spin_limit;
   int32_t* dev_err;
   int own_chunk;             // the chunk that needs no input flag
 };
 
-// Waits (one thread polls) until input chunk c is marked ready, then acquires
+// Waits (one thread polls) until input segment g is marked ready, then acquires
 // at system scope: the producer is another agent. Bounded: after spin_limit
 // polls the tile records MC2_DEVERR_TIMEOUT and goes on.
-__device__ __forceinline__ void wait_input_chunk(const ChunkedArgs& p, int c) {
+__device__ __forceinline__ void wait_input_segment(const ChunkedArgs& p, int g) {
   if (threadIdx.x == 0) {
     bool ready = false;
     for (uint32_t i = 0; i < p.spin_limit; ++i) {
-      if (__hip_atomic_load(p.in_flags + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
+      if (__hip_atomic_load(p.in_flags + g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) ==
           p.in_epoch) {
         ready = true;
         break;
@@ -180,27 +184,45 @@ __device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
 }
 
 // One output tile (or the row half `half` of one, for a TS of half height):
-// main loop, epilogue, store, and the chunk's ready flag. Tiles are numbered
+// main loop, epilogue, store, and the segment's ready flag. Tiles are numbered
 // chunk by chunk in the order the chunks are due (first_chunk,
-// first_chunk + 1, ... mod W), and inside a chunk row-block fastest, so that a
-// run of consecutive tiles forms a compact block of the chunk and the chunks
-// complete roughly in order. `weight` is the tile's share of the chunk
-// counter (2 for a whole tile, 1 for a half).
+// first_chunk + 1, ... mod W), inside a chunk piece by piece in row order, and
+// inside a piece row-block fastest, so that a run of consecutive tiles forms a
+// compact block and the segments complete roughly in order. `weight` is the
+// tile's share of the segment counter (2 for a whole tile, 1 for a half).
 template <Elem E, bool BT, class TS, Out O>
 __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, int tile, int half,
                                              uint32_t weight) {
   constexpr int OS = OutInfo<O>::bytes;
   const int seq = tile / p.tiles_per_chunk;
-  const int t = tile - seq * p.tiles_per_chunk;
+  int t = tile - seq * p.tiles_per_chunk;
   int c = p.first_chunk + seq;
   c = c >= p.world ? c - p.world : c;
-  const int tm = t % p.tiles_m, tn = t / p.tiles_m;
-  const int64_t row0 = c * p.mc + static_cast<int64_t>(tm) * (TS::BM << (weight == 1)) +
+  const int long_tiles = p.sr * p.tiles_long;
+  int j, tiles_mj, seg_tiles;
+  if (t < long_tiles) {
+    j = t / p.tiles_long;
+    t -= j * p.tiles_long;
+    tiles_mj = p.tiles_m1;
+    seg_tiles = p.tiles_long;
+  } else {
+    const int v = (t - long_tiles) / p.tiles_short;
+    j = p.sr + v;
+    t -= long_tiles + v * p.tiles_short;
+    tiles_mj = p.tiles_m0;
+    seg_tiles = p.tiles_short;
+  }
+  const int g = c * p.sub + j;
+  const int64_t seg_row0 = c * p.mc + j * p.sq + (j < p.sr ? j : p.sr);
+  const int64_t row_end = seg_row0 + p.sq + (j < p.sr ? 1 : 0);
+  const int tm = t % tiles_mj, tn = t / tiles_mj;
+  const int64_t row0 = seg_row0 + static_cast<int64_t>(tm) * (TS::BM << (weight == 1)) +
                        static_cast<int64_t>(half) * TS::BM;
-  const int64_t row_end = c * p.mc + p.mc;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
 
-  if (p.in_flags && c != p.own_chunk) wait_input_chunk(p, c);
+  if (p.in_flags && c != p.own_chunk) wait_input_segment(p, g);
+  // the lower half of a tile that overhangs its piece may hold no rows
+  if (row0 < row_end) {
   typename Mma<E>::acc_t acc[TS::FM][TS::FN];
   BDesc bd{p.B, p.ldb, p.n};
   PlainCols cm{col0, p.n - 16 / ElemInfo<E>::bytes};
@@ -223,6 +245,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
                                 if (r < nrows && cc < ncols) put_out_global<O>(base + r * p.ldo + cc * OS, v);
                               });
   }
+  }
 
   if (p.flags) {
     // Each wave waits for its own stores; after the barrier, thread 0's
@@ -235,12 +258,12 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
     __syncthreads();
     if (threadIdx.x == 0) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      const uint32_t prev = __hip_atomic_fetch_add(&p.counters[c], weight, __ATOMIC_RELAXED,
+      const uint32_t prev = __hip_atomic_fetch_add(&p.counters[g], weight, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
-      if (prev + weight == 2u * static_cast<uint32_t>(p.tiles_per_chunk)) {
+      if (prev + weight == 2u * static_cast<uint32_t>(seg_tiles)) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        __hip_atomic_store(&p.counters[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&p.flags[c], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(&p.counters[g], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&p.flags[g], p.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
       }
     }
   }
@@ -543,11 +566,17 @@ static bool half_tail(int64_t tiles, int64_t cus) {
   return rem > 0 && tiles > rem && 2 * rem <= cus;
 }
 
-static bool use_tall_tiles(int64_t mc, int64_t n, int W) {
+// Tiles of one chunk cut into `sub` pieces (sq rows, one more for the first
+// sr), for tiles of bm rows and tn tile columns.
+static int64_t chunk_tiles(int64_t sq, int sr, int sub, int bm, int64_t tn) {
+  return (sr * ((sq + bm) / bm) + (sub - sr) * ((sq + bm - 1) / bm)) * tn;
+}
+
+static bool use_tall_tiles(int64_t sq, int sr, int sub, int64_t n, int W) {
   const int64_t cus = num_cus();
   const int64_t tn = (n + 255) / 256;
-  const int64_t tl = ((mc + 255) / 256) * tn * W;
-  const int64_t tm = ((mc + 127) / 128) * tn * W;
+  const int64_t tl = chunk_tiles(sq, sr, sub, 256, tn) * W;
+  const int64_t tm = chunk_tiles(sq, sr, sub, 128, tn) * W;
   const int64_t rl = (tl + cus - 1) / cus, rm = (tm + cus - 1) / cus;
   const int64_t cost_l = half_tail(tl, cus) ? 4 * (rl - 1) + 3 : 4 * rl;
   return cost_l <= 3 * rm;
@@ -564,8 +593,8 @@ struct InputWait {
 static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
                        int first_chunk, int nsim, int x2_trans, int in_dtype, const void* bias,
                        const float* s1, const float* s2, int out_dtype, void* out,
-                       uint32_t* flags, uint32_t* counters, uint32_t epoch, hipStream_t stream,
-                       const InputWait& inw = InputWait{}) {
+                       uint32_t* flags, uint32_t* counters, uint32_t epoch, int sub,
+                       hipStream_t stream, const InputWait& inw = InputWait{}) {
   const int es = in_dtype == MC2_I8 ? 1 : 2;
   const int os = (out_dtype == MC2_F32 || out_dtype == MC2_I32) ? 4 : 2;
   ChunkedArgs a{};
@@ -589,11 +618,19 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
   a.mc = m / W;
   a.world = W;
   a.first_chunk = first_chunk;
-  const bool tall = use_tall_tiles(a.mc, n, W);
+  a.sub = sub;
+  a.sq = a.mc / sub;
+  a.sr = static_cast<int>(a.mc % sub);
+  const bool tall = use_tall_tiles(a.sq, a.sr, sub, n, W);
   const int BM = tall ? TileL::BM : TileM::BM;
-  a.tiles_m = static_cast<int>((a.mc + BM - 1) / BM);
+  a.tiles_m1 = static_cast<int>((a.sq + BM) / BM);
+  a.tiles_m0 = static_cast<int>((a.sq + BM - 1) / BM);
   a.tiles_n = static_cast<int>((n + 255) / 256);
-  a.tiles_per_chunk = a.tiles_m * a.tiles_n;
+  a.tiles_long = a.tiles_m1 * a.tiles_n;
+  a.tiles_short = a.tiles_m0 * a.tiles_n;
+  const int64_t per_chunk = chunk_tiles(a.sq, a.sr, sub, BM, a.tiles_n);
+  if (per_chunk * W > 0x3fffffff) return MC2_ERR_SHAPE;
+  a.tiles_per_chunk = static_cast<int>(per_chunk);
   a.round = static_cast<int>(num_cus() / 8 * 8);
   a.bias_mul = static_cast<float>(nsim);
   a.flags = flags;
@@ -640,7 +677,8 @@ extern "C" int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_
                                int world_size, int rank, int nsim, int x2_trans, int in_dtype,
                                const void* bias, const float* x1_scale, const float* x2_scale,
                                int out_dtype, void* out, uint32_t* ready_flags,
-                               uint32_t* flag_counters, uint32_t epoch, hipStream_t stream) {
+                               uint32_t* flag_counters, uint32_t epoch, int comm_turn,
+                               hipStream_t stream) {
   if (!x1 || !x2 || !out) return MC2_ERR_NULL;
   if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
   if (m <= 0 || n <= 0 || m % world_size) return MC2_ERR_SHAPE;
@@ -668,14 +706,17 @@ extern "C" int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_
   if (!offsets_fit(k * es, (x2_trans ? k : n) * es)) return MC2_ERR_UNSUPPORTED;
   if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
   if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+  if (comm_turn < 0 || comm_turn > m / world_size) return MC2_ERR_SHAPE;
   const int first = (rank + 1) % world_size;
   return run_chunked(x1, x2, m, k, n, world_size, first, nsim, x2_trans, in_dtype, bias, x1_scale,
-                     x2_scale, out_dtype, out, ready_flags, flag_counters, epoch, stream);
+                     x2_scale, out_dtype, out, ready_flags, flag_counters, epoch,
+                     comm_turn > 1 ? comm_turn : 1, stream);
 }
 
 static int check_ag(const void* x_gathered, const void* x2, int64_t m_c, int64_t k, int64_t n,
                     int world_size, int rank, int x2_trans, int in_dtype, void* out,
-                    uint32_t* ready_flags, uint32_t* flag_counters, uint32_t epoch) {
+                    uint32_t* ready_flags, uint32_t* flag_counters, uint32_t epoch,
+                    int comm_turn) {
   if (!x_gathered || !x2 || !out) return MC2_ERR_NULL;
   if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
   if (m_c <= 0 || n <= 0 || k <= 0) return MC2_ERR_SHAPE;
@@ -685,6 +726,7 @@ static int check_ag(const void* x_gathered, const void* x2, int64_t m_c, int64_t
   if (!offsets_fit(k * 2, (x2_trans ? k : n) * 2)) return MC2_ERR_UNSUPPORTED;
   if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
   if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+  if (comm_turn < 0 || comm_turn > m_c) return MC2_ERR_SHAPE;
   return MC2_OK;
 }
 
@@ -692,11 +734,11 @@ extern "C" int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, i
                                        int64_t k, int64_t n, int world_size, int rank,
                                        int x2_trans, int in_dtype, const void* bias, void* out,
                                        uint32_t* ready_flags, uint32_t* flag_counters,
-                                       uint32_t epoch, const uint32_t* in_flags,
+                                       uint32_t epoch, int comm_turn, const uint32_t* in_flags,
                                        uint32_t in_epoch, uint32_t spin_limit, int32_t* dev_err,
                                        hipStream_t stream) {
   const int st = check_ag(x_gathered, x2, m_c, k, n, world_size, rank, x2_trans, in_dtype, out,
-                          ready_flags, flag_counters, epoch);
+                          ready_flags, flag_counters, epoch, comm_turn);
   if (st) return st;
   if (!in_flags) return MC2_ERR_NULL;
   if (in_epoch == 0 || spin_limit == 0) return MC2_ERR_SHAPE;
@@ -707,25 +749,20 @@ extern "C" int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, i
   w.dev_err = dev_err;
   return run_chunked(x_gathered, x2, m_c * world_size, k, n, world_size, rank, 1, x2_trans,
                      in_dtype, bias, nullptr, nullptr, in_dtype, out, ready_flags, flag_counters,
-                     epoch, stream, w);
+                     epoch, comm_turn > 1 ? comm_turn : 1, stream, w);
 }
 
 extern "C" int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
                                int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
                                const void* bias, void* out, uint32_t* ready_flags,
-                               uint32_t* flag_counters, uint32_t epoch, hipStream_t stream) {
-  if (!x_gathered || !x2 || !out) return MC2_ERR_NULL;
-  if (!valid_world(world_size) || rank < 0 || rank >= world_size) return MC2_ERR_SHAPE;
-  if (m_c <= 0 || n <= 0 || k <= 0) return MC2_ERR_SHAPE;
-  if (in_dtype != MC2_F16 && in_dtype != MC2_BF16) return MC2_ERR_DTYPE;
-  if (k % 8 || n % 8) return MC2_ERR_ALIGN;
-  if (!aligned16(x_gathered) || !aligned16(x2) || !aligned16(out)) return MC2_ERR_ALIGN;
-  if (!offsets_fit(k * 2, (x2_trans ? k : n) * 2)) return MC2_ERR_UNSUPPORTED;
-  if ((ready_flags == nullptr) != (flag_counters == nullptr)) return MC2_ERR_NULL;
-  if (ready_flags && epoch == 0) return MC2_ERR_SHAPE;
+                               uint32_t* flag_counters, uint32_t epoch, int comm_turn,
+                               hipStream_t stream) {
+  const int st = check_ag(x_gathered, x2, m_c, k, n, world_size, rank, x2_trans, in_dtype, out,
+                          ready_flags, flag_counters, epoch, comm_turn);
+  if (st) return st;
   return run_chunked(x_gathered, x2, m_c * world_size, k, n, world_size, rank, 1, x2_trans,
                      in_dtype, bias, nullptr, nullptr, in_dtype, out, ready_flags, flag_counters,
-                     epoch, stream);
+                     epoch, comm_turn > 1 ? comm_turn : 1, stream);
 }
 
 // ---------------------------------------------------------------- MatmulAllReduce
@@ -788,7 +825,7 @@ extern "C" int mc2_mm_ar_local(const void* x1, const void* x2, int64_t m, int64_
   const int W = world_size;
   if (rounding == MC2_AR_ONE_ROUNDING)  // all W partials in one accumulator, all rows kept
     return run_chunked(x1, x2, m, k, n, 1, 0, W, x2_trans, in_dtype, bias, nullptr, nullptr,
-                       in_dtype, out, nullptr, nullptr, 0, stream);
+                       in_dtype, out, nullptr, nullptr, 0, 1, stream);
   const size_t need = mc2_mm_ar_workspace_size(m, n, W, in_dtype, rounding);
   if (!workspace) return MC2_ERR_NULL;
   if (!aligned16(workspace)) return MC2_ERR_ALIGN;
@@ -799,7 +836,7 @@ extern "C" int mc2_mm_ar_local(const void* x1, const void* x2, int64_t m, int64_
                                static_cast<const char*>(x2) + static_cast<int64_t>(w) * k * n * 2,
                                m, k, n, 1, 0, 1, x2_trans, in_dtype, bias, nullptr, nullptr,
                                in_dtype, static_cast<char*>(workspace) + static_cast<int64_t>(w) * m * n * 2,
-                               nullptr, nullptr, 0, stream);
+                               nullptr, nullptr, 0, 1, stream);
     if (st) return st;
   }
   return launch_ar_sum(workspace, W, m * n, in_dtype, rounding, out, stream);

@@ -60,12 +60,28 @@ def mc2_version() -> str:
     return _lib.load().mc2_version().decode()
 
 
+def _check_flags(world_size, comm_turn, ready_flags, flag_counters):
+    """Flag arrays hold one uint32 per segment: world_size * max(comm_turn, 1).
+    The counters live on the GPU; the ready flags on the GPU or in host-pinned
+    memory (for a host-side consumer)."""
+    segs = world_size * max(int(comm_turn), 1)
+    for a in (ready_flags, flag_counters):
+        if a is not None and (a.dtype not in (torch.int32, torch.uint32) or a.numel() < segs
+                              or not a.is_contiguous()):
+            raise ValueError(f"flag arrays must hold {segs} int32 (world_size * max(comm_turn, 1))")
+    if flag_counters is not None and not flag_counters.is_cuda:
+        raise ValueError("flag_counters must be on the GPU")
+    if ready_flags is not None and not (ready_flags.is_cuda or ready_flags.is_pinned()):
+        raise ValueError("ready_flags must be GPU or host-pinned memory")
+
+
 def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_scale=None,
                     x2_scale=None, out_dtype=None, out=None, ready_flags=None,
-                    flag_counters=None, epoch=0):
+                    flag_counters=None, epoch=0, comm_turn=0):
     """MatmulReduceScatter compute share; x1 (m, k) or stacked (nsim, m, k),
     x2 (k, n) / (n, k) or stacked. Returns out (m, n)."""
-    dev = _dev(x1, x2, bias, x1_scale, x2_scale, out, ready_flags, flag_counters)
+    dev = _dev(x1, x2, bias, x1_scale, x2_scale, out, flag_counters)
+    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     nsim = 1 if x1.dim() == 2 else x1.shape[0]
     m, k = x1.shape[-2], x1.shape[-1]
     n = x2.shape[-2] if x2_trans else x2.shape[-1]
@@ -82,15 +98,16 @@ def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_s
     st = _lib.load().mc2_mm_rs_local(
         x1.data_ptr(), x2.data_ptr(), m, k, n, world_size, rank, nsim, int(bool(x2_trans)),
         _CODES[x1.dtype], _ptr(bias), _ptr(x1_scale), _ptr(x2_scale), _CODES[out_dtype],
-        out.data_ptr(), _ptr(ready_flags), _ptr(flag_counters), epoch, _stream(dev))
+        out.data_ptr(), _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, _stream(dev))
     _check("mc2_mm_rs_local", st)
     return out
 
 
 def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=None, out=None,
-                    ready_flags=None, flag_counters=None, epoch=0):
+                    ready_flags=None, flag_counters=None, epoch=0, comm_turn=0):
     """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out."""
-    dev = _dev(x_gathered, x2, bias, out, ready_flags, flag_counters)
+    dev = _dev(x_gathered, x2, bias, out, flag_counters)
+    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     M, k = x_gathered.shape
     if M % world_size:
         raise ValueError("rows of x_gathered must be world_size * m_c")
@@ -100,22 +117,25 @@ def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=No
     st = _lib.load().mc2_ag_mm_local(
         x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
         int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
-        _ptr(ready_flags), _ptr(flag_counters), epoch, _stream(dev))
+        _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, _stream(dev))
     _check("mc2_ag_mm_local", st)
     return out
 
 
 def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch, *,
                             spin_limit=1 << 24, x2_trans=False, bias=None, out=None,
-                            ready_flags=None, flag_counters=None, epoch=0, dev_err=None):
-    """mc2_ag_mm_local whose tiles wait until in_flags[c] == in_epoch before
-    reading gathered chunk c (c != rank). in_flags: W int32 on the GPU or in
-    host-pinned memory."""
-    if in_flags.dtype not in (torch.int32, torch.uint32) or in_flags.numel() != world_size:
-        raise ValueError("in_flags must hold world_size int32")
+                            ready_flags=None, flag_counters=None, epoch=0, dev_err=None,
+                            comm_turn=0):
+    """mc2_ag_mm_local whose tiles wait until in_flags[g] == in_epoch before
+    reading segment g of a gathered chunk other than the own one. in_flags:
+    world_size * max(comm_turn, 1) int32 on the GPU or in host-pinned memory."""
+    segs = world_size * max(int(comm_turn), 1)
+    if in_flags.dtype not in (torch.int32, torch.uint32) or in_flags.numel() != segs:
+        raise ValueError(f"in_flags must hold {segs} int32")
+    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     if not in_flags.is_cuda and not in_flags.is_pinned():
         raise ValueError("in_flags must be GPU or host-pinned memory")
-    dev = _dev(x_gathered, x2, bias, out, ready_flags, flag_counters, dev_err)
+    dev = _dev(x_gathered, x2, bias, out, flag_counters, dev_err)
     M, k = x_gathered.shape
     if M % world_size:
         raise ValueError("rows of x_gathered must be world_size * m_c")
@@ -125,7 +145,7 @@ def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch
     st = _lib.load().mc2_ag_mm_local_inflags(
         x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
         int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
-        _ptr(ready_flags), _ptr(flag_counters), epoch, in_flags.data_ptr(), in_epoch,
+        _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, in_flags.data_ptr(), in_epoch,
         spin_limit, _ptr(dev_err), _stream(dev))
     _check("mc2_ag_mm_local_inflags", st)
     return out

@@ -101,18 +101,26 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
  *
  * Chunk schedule and ready flags: chunks are computed in the order
  * (rank + 1 + i) mod W, i = 0..W-1, so that the chunk this rank keeps comes
- * last. When ready_flags is not NULL, flag_counters must point to W uint32
- * that are zero before the first call (the library leaves them zero after
- * each call); the last tile to finish chunk c stores ready_flags[c] = epoch
- * with release ordering at system scope once every byte of chunk c is
+ * last. comm_turn is the split granularity [RS "参数说明": comm_turn, of which
+ * that version accepts only 0]: 0 (the default) or 1 keeps each chunk whole;
+ * S > 1 cuts every chunk of m_c = m/W rows into S pieces of q = m_c / S rows
+ * in row order, one more row for each of the first m_c % S pieces, and each
+ * piece (segment g = c*S + j) gets its own ready flag; 1 <= S <= m_c, else
+ * MC2_ERR_SHAPE. Pieces are computed chunk by chunk in the order above, in
+ * row order inside a chunk. With G = W * max(comm_turn, 1) segments: when
+ * ready_flags is not NULL, ready_flags and flag_counters point to G uint32,
+ * the counters in device memory and zero before the first call (the library
+ * leaves them zero after each call), the flags in device or host-pinned
+ * memory; the last tile to finish segment g stores ready_flags[g] = epoch
+ * with release ordering at system scope once every byte of segment g is
  * visible. epoch must be nonzero and should differ between calls. Both flag
- * pointers NULL disables flags.
+ * pointers NULL disables flags. Results do not depend on comm_turn.
  */
 int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
                     int world_size, int rank, int nsim, int x2_trans, int in_dtype,
                     const void* bias, const float* x1_scale, const float* x2_scale,
                     int out_dtype, void* out, uint32_t* ready_flags,
-                    uint32_t* flag_counters, uint32_t epoch, hipStream_t stream);
+                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, hipStream_t stream);
 
 /*
  * mc2_ag_mm_local -- AllGatherMatmul compute share [AG]: out = allgather(x1) @ x2
@@ -123,24 +131,28 @@ int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_
  *   (MC2_F16 or MC2_BF16). out (W*m_c, n) in_dtype.
  *
  * Chunks are computed in the order (rank + i) mod W, starting with the chunk
- * this rank owns. Ready flags as for mc2_mm_rs_local. Constraints: k >= 1,
- * k % 8 == 0, n % 8 == 0, m_c >= 1, world_size in {1, 2, 4, 8, 16, 32}.
+ * this rank owns. comm_turn pieces and ready flags as for mc2_mm_rs_local
+ * (W * max(comm_turn, 1) segments, 0 <= comm_turn <= m_c). Constraints:
+ * k >= 1, k % 8 == 0, n % 8 == 0, m_c >= 1, world_size in {1, 2, 4, 8, 16, 32}.
  */
 int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
                     int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
                     const void* bias, void* out, uint32_t* ready_flags,
-                    uint32_t* flag_counters, uint32_t epoch, hipStream_t stream);
+                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, hipStream_t stream);
 
 /*
  * mc2_ag_mm_local_inflags -- mc2_ag_mm_local whose tiles wait for their input
- * chunk: the consumer side of the AllGatherMatmul pipeline [AG, CANN hccl
+ * segment: the consumer side of the AllGatherMatmul pipeline [AG, CANN hccl
  * issue 158; MC2 "执行路径": communication and computation of different chunks
- * overlap]. Before a tile reads gathered chunk c (c != rank: the own chunk is
- * local), one thread polls in_flags[c] until it equals in_epoch, then takes
- * a system-scope acquire fence, so every byte written to chunk c before the
- * producer's release of in_flags[c] is visible.
+ * overlap]. Input arrives at the granularity of the output segments
+ * (comm_turn pieces, segment g = c*S + j as for mc2_mm_rs_local). Before a
+ * tile reads segment g of gathered chunk c (c != rank: the own chunk is
+ * local), one thread polls in_flags[g] until it equals in_epoch, then takes
+ * a system-scope acquire fence, so every byte written to that segment before
+ * the producer's release of in_flags[g] is visible.
  *
- *   in_flags   W uint32 in memory the GPU can read (device, or host-pinned);
+ *   in_flags   W * max(comm_turn, 1) uint32 in memory the GPU can read
+ *              (device, or host-pinned);
  *              written by an agent that does not need this kernel to make
  *              progress (a copy engine, a peer, the host): the kernel never
  *              raises them itself, so it cannot deadlock on them.
@@ -157,7 +169,8 @@ int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t
 int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
                             int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
                             const void* bias, void* out, uint32_t* ready_flags,
-                            uint32_t* flag_counters, uint32_t epoch, const uint32_t* in_flags,
+                            uint32_t* flag_counters, uint32_t epoch, int comm_turn,
+                            const uint32_t* in_flags,
                             uint32_t in_epoch, uint32_t spin_limit, int32_t* dev_err,
                             hipStream_t stream);
 

@@ -47,11 +47,13 @@ def test_version_and_status_strings(lib):
 
 def rs(lib, **over):
     a = dict(x1=FAKE, x2=FAKE, m=128, k=512, n=64, W=2, rank=0, nsim=1, trans=0, dt=F16,
-             bias=None, s1=None, s2=None, odt=F16, out=FAKE, flags=None, cnt=None, epoch=0)
+             bias=None, s1=None, s2=None, odt=F16, out=FAKE, flags=None, cnt=None, epoch=0,
+             turn=0)
     a.update(over)
     return lib.mc2_mm_rs_local(a["x1"], a["x2"], a["m"], a["k"], a["n"], a["W"], a["rank"],
                                a["nsim"], a["trans"], a["dt"], a["bias"], a["s1"], a["s2"],
-                               a["odt"], a["out"], a["flags"], a["cnt"], a["epoch"], None)
+                               a["odt"], a["out"], a["flags"], a["cnt"], a["epoch"], a["turn"],
+                               None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -77,6 +79,8 @@ def rs(lib, **over):
     (dict(x1=FAKE + 8), ERR_ALIGN),
     (dict(flags=FAKE), ERR_NULL),         # flags need counters
     (dict(flags=FAKE, cnt=FAKE, epoch=0), ERR_SHAPE),
+    (dict(turn=-1), ERR_SHAPE),           # comm_turn >= 0
+    (dict(turn=65), ERR_SHAPE),           # at most m / W pieces (64 rows per chunk)
 ])
 def test_mm_rs_rejects(lib, over, code):
     assert rs(lib, **over) == code
@@ -84,11 +88,14 @@ def test_mm_rs_rejects(lib, over, code):
 
 def test_ag_mm_rejects(lib):
     f = lib.mc2_ag_mm_local
-    assert f(None, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_NULL
-    assert f(FAKE, FAKE, 16, 512, 64, 8, 8, 0, BF16, None, FAKE, None, None, 0, None) == ERR_SHAPE
-    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, I8, None, FAKE, None, None, 0, None) == ERR_DTYPE
-    assert f(FAKE, FAKE, 16, 500, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_ALIGN
-    assert f(FAKE, FAKE, 0, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, None) == ERR_SHAPE
+    tail = (None, None, 0, 0, None)
+    assert f(None, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_NULL
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 8, 0, BF16, None, FAKE, *tail) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, I8, None, FAKE, *tail) == ERR_DTYPE
+    assert f(FAKE, FAKE, 16, 500, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_ALIGN
+    assert f(FAKE, FAKE, 0, 512, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, 17, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, -1, None) == ERR_SHAPE
 
 
 def test_moe_entry_points_reject(lib):
@@ -119,12 +126,13 @@ def test_moe_entry_points_reject(lib):
 
 def test_ag_mm_inflags_validates(lib):
     f = lib.mc2_ag_mm_local_inflags
-    base = (FAKE, FAKE, 100, 512, 264, 8, 0, 0, BF16, None, FAKE, None, None, 0)
+    base = (FAKE, FAKE, 100, 512, 264, 8, 0, 0, BF16, None, FAKE, None, None, 0, 0)
     assert f(*base, None, 1, 100, None, None) == ERR_NULL      # in_flags required
     assert f(*base, FAKE, 0, 100, None, None) == ERR_SHAPE     # in_epoch != 0
     assert f(*base, FAKE, 1, 0, None, None) == ERR_SHAPE       # spin_limit >= 1
     assert f(None, *base[1:], FAKE, 1, 100, None, None) == ERR_NULL
     assert f(*base[:8], I8, *base[9:], FAKE, 1, 100, None, None) == ERR_DTYPE
+    assert f(*base[:14], 101, FAKE, 1, 100, None, None) == ERR_SHAPE   # comm_turn <= m_c
 
 
 def test_mm_ar_validates(lib):
