@@ -26,6 +26,20 @@ Readings where the page is silent (each listed with the design notes):
 * with a single source rank the received rows of local expert g are the send
   buffer's rows of expert ep_rank * E_l + g, and the combine writes its result
   back over those same rows.
+
+Backward (same page, "PR 改动": the two autograd Functions wrap the fused
+operator in forward and backward; "验证项": the fc1 / fc2 gradients are
+compared against the plain alltoall path). The page gives no formulas; the
+gradients are those of the forward above, with these readings:
+
+* the combine's input gradient comes back in the combine buffer's layout (the
+  rows the send buffer used), and the dispatch's input gradient goes out in
+  the send buffer's layout, as the reverse AllToAllv would move them;
+* SwiGLU's backward uses the fc1 pre-activation as the forward stored it
+  (bf16) and the unrounded fc2 input gradient; the gradients handed between
+  stages (fc2 input, fc1 output, fc1 input) are stored as bf16;
+* weight gradients are kept in float (fp32 on the device) and not rounded to
+  bf16.
 """
 from __future__ import annotations
 
@@ -211,3 +225,79 @@ def moe_local(x, sel, probs, w1, w2, *, num_experts, ep_rank, local_experts,
                      w2=w2, combine_buf=buf)
     out = unpermute(y_full, p["unpermute_idx"], probs, T, K)
     return {"counts": counts, "permute": p, "h": h, "y_full": y_full, "out": out}
+
+
+# --------------------------------------------------------------------------
+# Backward
+# --------------------------------------------------------------------------
+
+def swiglu_backward(a, dh):
+    """Gradient of SwiGLU at the pre-activation ``a`` (rows, 2I), for the
+    output gradient ``dh`` (rows, I): (rows, 2I) holding
+    dh * up * silu'(gate) in the gate columns and dh * silu(gate) in the up
+    columns, where silu'(g) = s * (1 + g * (1 - s)) with s = 1 / (1 + e^-g)."""
+    a = np.asarray(a, dtype=np.float64)
+    inter = a.shape[1] // 2
+    gate, up = a[:, :inter], a[:, inter:]
+    with np.errstate(over="ignore"):
+        s = 1.0 / (1.0 + np.exp(-gate))
+    return np.concatenate([dh * up * (s * (1.0 + gate * (1.0 - s))), dh * (gate * s)], axis=1)
+
+
+def gmm_backward(rows, group_sizes, weights, dy):
+    """Gradients of the grouped matmul Y_g = X_g @ W_g for the output gradient
+    ``dy``: dX_g = dY_g @ W_g^T and dW_g = X_g^T @ dY_g, group after group,
+    in float64 (unrounded). ``rows``, ``weights`` and ``dy`` are float64
+    values. Returns (dX (rows, K), dW (G, K, N))."""
+    X = np.asarray(rows, dtype=np.float64)
+    Wt = np.asarray(weights, dtype=np.float64)
+    D = np.asarray(dy, dtype=np.float64)
+    dX = np.zeros((X.shape[0], Wt.shape[1]))
+    dW = np.zeros(Wt.shape)
+    off = 0
+    for g, cnt in enumerate(int(c) for c in group_sizes):
+        dX[off:off + cnt] = D[off:off + cnt] @ Wt[g].T
+        dW[g] = X[off:off + cnt].T @ D[off:off + cnt]
+        off += cnt
+    return dX, dW
+
+
+def combine_backward(dy_buf, recv_counts, send_counts, *, ep_rank, local_experts, w2, h,
+                     g_saved=None, act="none", dtype="bf16"):
+    """Backward of the combine segment (GroupedMatmul fc2 -> AllToAllv).
+
+    ``dy_buf`` holds the output gradient in the combine buffer's layout
+    (bf16); this rank's rows are those ``combine`` wrote. ``h`` holds the fc2
+    inputs (bf16, group after group from row 0). Returns (dgrad, dW2):
+    dW2[g] = h_g^T @ dY_g (float64) and dgrad, the gradient of the fc2 input
+    (act 'none') or, with act 'swiglu', of the fc1 pre-activation
+    ``g_saved`` (bf16, rows x 2I) through SwiGLU. dgrad is rounded to
+    ``dtype`` (None: unrounded)."""
+    check_counts(send_counts, recv_counts, ep_rank, local_experts)
+    start, n = local_slice(send_counts, ep_rank, local_experts)
+    dY = decode(np.asarray(dy_buf)[start:start + n], "bf16")
+    Hv = decode(np.asarray(h)[:n], "bf16")
+    dA, dW2 = gmm_backward(Hv, recv_counts, decode(w2, "bf16"), dY)
+    if act == "swiglu":
+        dA = swiglu_backward(decode(np.asarray(g_saved)[:n], "bf16"), dA)
+    elif act != "none":
+        raise ValueError(act)
+    return (round_to(dA, dtype) if dtype else dA), dW2
+
+
+def dispatch_backward(dg, recv_counts, send_counts, *, ep_rank, local_experts, w1, send_buf,
+                      dx_buf, dtype="bf16"):
+    """Backward of the dispatch segment (AllToAllv -> GroupedMatmul fc1).
+
+    ``dg`` holds the gradient of the fc1 output (bf16, group after group from
+    row 0). Returns (dx, dW1): dW1[g] = R_g^T @ dG_g (float64) over this
+    rank's rows R of ``send_buf``, and dx, a float64 copy of ``dx_buf`` whose
+    rows of this rank (the send buffer's) hold dG_g @ W1_g^T rounded to
+    ``dtype`` (None: unrounded)."""
+    check_counts(send_counts, recv_counts, ep_rank, local_experts)
+    start, n = local_slice(send_counts, ep_rank, local_experts)
+    R = decode(np.asarray(send_buf)[start:start + n], "bf16")
+    dX, dW1 = gmm_backward(R, recv_counts, decode(w1, "bf16"), decode(np.asarray(dg)[:n], "bf16"))
+    out = np.array(dx_buf, dtype=np.float64, copy=True)
+    out[start:start + n] = round_to(dX, dtype) if dtype else dX
+    return out, dW1

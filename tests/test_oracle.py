@@ -384,6 +384,91 @@ def test_gmm_brute_force_ragged_and_empty_groups():
         off += cnt
 
 
+def test_swiglu_backward_closed_forms():
+    """At gate 0: s = 1/2, silu = 0, silu' = 1/2. Large gate: silu' -> 1 and
+    silu -> g. Very negative gate: both vanish. Catches a dropped term of
+    silu' or swapped gate / up columns."""
+    dh = np.array([[2.0, -3.0]])
+    got = moe.swiglu_backward(np.array([[0.0, 0.0, 5.0, 7.0]]), dh)
+    np.testing.assert_array_equal(got, [[5.0, -10.5, 0.0, 0.0]])
+    got = moe.swiglu_backward(np.array([[40.0, 3.0]]), np.array([[1.5]]))
+    np.testing.assert_allclose(got, [[4.5, 60.0]], rtol=1e-12)
+    got = moe.swiglu_backward(np.array([[-60.0, 3.0]]), np.array([[1.5]]))
+    assert np.all(np.abs(got) < 1e-20)
+    # g = 1: silu' = s (1 + (1 - s)) with s = 1 / (1 + e^-1)
+    s = 1.0 / (1.0 + math.exp(-1.0))
+    got = moe.swiglu_backward(np.array([[1.0, 2.0]]), np.array([[1.0]]))
+    np.testing.assert_allclose(got, [[2.0 * s * (2.0 - s), s]], rtol=1e-15)
+
+
+def _leaf(a):
+    return torch.tensor(np.asarray(a, dtype=np.float64), requires_grad=True)
+
+
+def test_gmm_backward_matches_autograd():
+    """dX = dY W^T and dW = X^T dY per group against torch autograd in float64,
+    ragged and empty groups, non-square K x N (a transposed operand fails)."""
+    rng = np.random.default_rng(5)
+    sizes, K, N = [3, 0, 5, 1], 6, 4
+    X = rng.standard_normal((9, K))
+    W = rng.standard_normal((4, K, N))
+    dY = rng.standard_normal((9, N))
+    dX, dW = moe.gmm_backward(X, sizes, W, dY)
+    Xt, Wt = _leaf(X), _leaf(W)
+    outs, off = [], 0
+    for g, c in enumerate(sizes):
+        outs.append(Xt[off:off + c] @ Wt[g])
+        off += c
+    (torch.cat(outs) * torch.tensor(dY)).sum().backward()
+    np.testing.assert_allclose(dX, Xt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-12, atol=1e-12)
+    assert not dW[1].any()
+
+
+def test_moe_backward_chain_matches_autograd():
+    """The combine and dispatch backward on ep_rank 1 of 2 (E = 4, E_l = 2),
+    with bf16-stored inputs: each stage equals torch autograd of the forward
+    stage it inverts (fc2 on the stored h, SwiGLU on the stored
+    pre-activation, fc1 on the send rows), and only this rank's rows of the
+    input-gradient buffer change."""
+    rng = np.random.default_rng(6)
+    send_counts = np.array([2, 3, 4, 5])
+    recv = send_counts[2:4]
+    H, I, n = 16, 8, 9
+    bf = lambda shape, sd=1.0: wl.encode_bf16((rng.standard_normal(shape) * sd).astype(np.float32))
+    send_buf, dy_buf = bf((14, H)), bf((14, H))
+    w1, w2 = bf((2, H, 2 * I), 0.3), bf((2, I, H), 0.3)
+    g_saved, h = bf((n, 2 * I), 2.0), bf((n, I))
+    dec = lambda b: numerics.decode(b, "bf16")
+
+    dgrad, dW2 = moe.combine_backward(dy_buf, recv, send_counts, ep_rank=1, local_experts=2,
+                                      w2=w2, h=h, g_saved=g_saved, act="swiglu", dtype=None)
+    hl, w2l, gl = _leaf(dec(h)), _leaf(dec(w2)), _leaf(dec(g_saved))
+    dY = torch.tensor(dec(dy_buf)[5:14])
+    y = torch.cat([hl[:4] @ w2l[0], hl[4:] @ w2l[1]])
+    (y * dY).sum().backward()
+    np.testing.assert_allclose(dW2, w2l.grad.numpy(), rtol=1e-12, atol=1e-12)
+    act = torch.nn.functional.silu(gl[:, :I]) * gl[:, I:]
+    (act * hl.grad).sum().backward()
+    np.testing.assert_allclose(dgrad, gl.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+    dg = bf((n, 2 * I))
+    rest = rng.standard_normal((14, H))
+    dx, dW1 = moe.dispatch_backward(dg, recv, send_counts, ep_rank=1, local_experts=2, w1=w1,
+                                    send_buf=send_buf, dx_buf=rest, dtype=None)
+    xl, w1l = _leaf(dec(send_buf)[5:14]), _leaf(dec(w1))
+    a = torch.cat([xl[:4] @ w1l[0], xl[4:] @ w1l[1]])
+    (a * torch.tensor(dec(dg))).sum().backward()
+    np.testing.assert_allclose(dW1, w1l.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(dx[5:14], xl.grad.numpy(), rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(dx[:5], rest[:5])
+
+    # the plain fc2 backward (no SwiGLU) is the fc2 input gradient itself
+    dA, _ = moe.combine_backward(dy_buf, recv, send_counts, ep_rank=1, local_experts=2, w2=w2,
+                                 h=h, act="none", dtype=None)
+    np.testing.assert_allclose(dA, hl.grad.numpy(), rtol=1e-12, atol=1e-12)
+
+
 def test_dispatch_combine_slice_for_nonzero_rank():
     """ep_rank = 1 of 2 (E = 4, E_l = 2): the local rows start after experts
     0 and 1, and the combine writes exactly those rows."""

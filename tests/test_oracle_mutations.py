@@ -135,3 +135,37 @@ def test_pieces_before_chunks_is_caught(monkeypatch):
         return [(c, j) for j in range(max(s, 1)) for c in gemm.chunk_order(W, rank, kind)]
     monkeypatch.setattr(gemm, "segment_order", piece_major)
     _fails(pins.test_segment_order)
+
+
+def test_dsilu_without_curvature_term_is_caught(monkeypatch):
+    def flat(a, dh):
+        a = np.asarray(a, dtype=np.float64)
+        inter = a.shape[1] // 2
+        g, u = a[:, :inter], a[:, inter:]
+        s = 1.0 / (1.0 + np.exp(-g))
+        return np.concatenate([dh * u * s, dh * g * s], axis=1)
+    monkeypatch.setattr(moe, "swiglu_backward", flat)
+    _fails(pins.test_swiglu_backward_closed_forms)
+
+
+def test_weight_used_untransposed_in_dgrad_is_caught(monkeypatch):
+    real = moe.gmm_backward
+
+    def no_transpose(rows, sizes, weights, dy):
+        dX, dW = real(rows, sizes, weights, dy)
+        Wt = np.asarray(weights, dtype=np.float64)
+        D = np.asarray(dy, dtype=np.float64)
+        off = 0
+        for g, c in enumerate(int(x) for x in sizes):
+            k = min(Wt.shape[1], Wt.shape[2])
+            dX[off:off + c, :k] = D[off:off + c, :k] @ Wt[g][:k, :k]
+            off += c
+        return dX, dW
+    monkeypatch.setattr(moe, "gmm_backward", no_transpose)
+    _fails(pins.test_gmm_backward_matches_autograd)
+
+
+def test_combine_backward_reading_rows_from_zero_is_caught(monkeypatch):
+    real = moe.local_slice
+    monkeypatch.setattr(moe, "local_slice", lambda sc, r, el: (0, real(sc, r, el)[1]))
+    _fails(pins.test_moe_backward_chain_matches_autograd)
