@@ -12,7 +12,7 @@ sample of the headline workload.
 Inputs are seeded synthetic data resident in HBM before timing starts. Times
 come from HIP events on the stream the kernels are launched on.
 
-    python bench.py [--steps K] [--warmup W] [--only c2|c3|c4|c5a|c5b|split|all]
+    python bench.py [--steps K] [--warmup W] [--only c2|c3|c4|c4bwd|c5a|c5b|split|all]
                     [--no-cpu-baseline] [--calib-copy]
 """
 from __future__ import annotations
@@ -256,6 +256,55 @@ def main():
         }
         log("C4 MoE:", json.dumps(rows["c4_moe_ep_local"]))
         del x, perm, h, buf, y, w1, w2
+
+    # ---------------------------------------------------------------- C4 backward
+    if only in ("all", "c4bwd"):
+        # backward of the local expert FFN on the C4 shapes and router counts;
+        # the stored activations and incoming gradients are seeded stand-ins
+        log("C4 backward: generating inputs")
+        d = wl.c4_inputs()
+        E, E_l, H, I = d["E"], d["E_l"], d["H"], d["I"]
+        sel = to_dev(d["sel"])
+        counts = mc2.mc2_moe_histc(sel, E)
+        recv = counts[:E_l].clone()
+        n_loc = int(recv.sum().item())
+        bi = wl.moe_backward_inputs(1006, n_loc, H, I)
+        t = {k: to_dev(v, True) for k, v in bi.items()}
+        w1, w2 = to_dev(d["w1"], True), to_dev(d["w2"], True)
+        dgrad = torch.empty((n_loc, 2 * I), dtype=torch.bfloat16, device=dev)
+        dw2 = torch.empty((E_l, I, H), dtype=torch.float32, device=dev)
+        dx = torch.empty((n_loc, H), dtype=torch.bfloat16, device=dev)
+        dw1 = torch.empty((E_l, H, 2 * I), dtype=torch.float32, device=dev)
+        ws_c = torch.empty(mc2.mc2_gmm_backward_workspace_size(n_loc, E_l, I, H), dtype=torch.uint8,
+                           device=dev)
+        ws_d = torch.empty(mc2.mc2_gmm_backward_workspace_size(n_loc, E_l, H, 2 * I), dtype=torch.uint8,
+                           device=dev)
+        err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+        def f_cb():
+            mc2.mc2_gmm_combine_backward(t["dy"], recv, counts, w2, t["h"], ep_rank=0,
+                                         num_experts=E, act=mc2.MC2_ACT_SWIGLU, g_saved=t["g"],
+                                         dgrad_out=dgrad, dw2_out=dw2, workspace=ws_c, dev_err=err)
+
+        def f_db():
+            mc2.mc2_gmm_dispatch_backward(t["dg"], recv, counts, w1, t["send"], dx, ep_rank=0,
+                                          num_experts=E, dw1_out=dw1, workspace=ws_d, dev_err=err)
+
+        f_cb()
+        f_db()
+        torch.cuda.synchronize()
+        assert err.item() == 0
+        t_cb = timed(f_cb, 100, 10)
+        t_db = timed(f_db, 100, 10)
+        fl_cb = 4.0 * n_loc * I * H
+        fl_db = 4.0 * n_loc * 2 * I * H
+        tf = (fl_cb + fl_db) / (t_cb + t_db) / 1e9
+        rows["c4_moe_backward"] = {
+            "n_loc": n_loc, "fc2_backward_us": t_cb * 1e3, "fc1_backward_us": t_db * 1e3,
+            "fc2_backward_TFLOP/s": fl_cb / t_cb / 1e9, "fc1_backward_TFLOP/s": fl_db / t_db / 1e9,
+            "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+        log("C4 backward:", json.dumps(rows["c4_moe_backward"]))
+        del t, w1, w2, dgrad, dw2, dx, dw1, ws_c, ws_d
 
     # ---------------------------------------------------------------- C5
     if only in ("all", "c5a", "c5b"):

@@ -28,6 +28,11 @@ SIGNATURES = {
     "mc2_gmm_dispatch": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _I, _P, _I64, _P,
                               _P]),
     "mc2_gmm_combine": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _P, _I64, _P, _P]),
+    "mc2_gmm_backward_workspace_size": (C.c_size_t, [_I64, _I, _I64, _I64]),
+    "mc2_gmm_combine_backward": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _P, _I64,
+                                      _P, _I, _P, _P, _P, C.c_size_t, _P, _P]),
+    "mc2_gmm_dispatch_backward": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _P,
+                                       _I64, _P, _I64, _P, _P, C.c_size_t, _P, _P]),
     "mc2_moe_unpermute": (_I, [_P, _I64, _P, _P, _I64, _I, _I64, _P, _P, _P]),
     "mc2_status_string": (C.c_char_p, [_I]),
     "mc2_version": (C.c_char_p, []),

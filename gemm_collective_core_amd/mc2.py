@@ -271,6 +271,62 @@ def mc2_gmm_combine(h, recv_counts, send_counts, w2, combine_buf, *, ep_rank, nu
     return combine_buf
 
 
+def mc2_gmm_backward_workspace_size(rows, local_experts, M, N) -> int:
+    return int(_lib.load().mc2_gmm_backward_workspace_size(rows, local_experts, M, N))
+
+
+def _workspace(nbytes, workspace, dev):
+    if workspace is None:
+        return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    return workspace
+
+
+def mc2_gmm_combine_backward(dy_buf, recv_counts, send_counts, w2, h, *, ep_rank, num_experts,
+                             act=MC2_ACT_NONE, g_saved=None, world_size_src=1, dgrad_out=None,
+                             dw2_out=None, workspace=None, dev_err=None):
+    """Backward of the grouped fc2: returns (dgrad, dW2). dgrad is the fc2
+    input gradient (rows of h, I), or with act=MC2_ACT_SWIGLU the gradient of
+    the saved fc1 pre-activation g_saved (rows, 2I); dW2 (E_l, I, H) fp32."""
+    dev = _dev(dy_buf, recv_counts, send_counts, w2, h, g_saved, dgrad_out, dw2_out, workspace,
+               dev_err)
+    E_l, I, H = w2.shape
+    if dgrad_out is None:
+        cols = 2 * I if act == MC2_ACT_SWIGLU else I
+        dgrad_out = torch.empty((h.shape[0], cols), dtype=torch.bfloat16, device=dev)
+    if dw2_out is None:
+        dw2_out = torch.empty((E_l, I, H), dtype=torch.float32, device=dev)
+    need = mc2_gmm_backward_workspace_size(h.shape[0], E_l, I, H)
+    workspace = _workspace(need, workspace, dev)
+    st = _lib.load().mc2_gmm_combine_backward(
+        dy_buf.data_ptr(), dy_buf.shape[0], recv_counts.data_ptr(), send_counts.data_ptr(),
+        world_size_src, ep_rank, num_experts, E_l, w2.data_ptr(), I, H, h.data_ptr(), h.shape[0],
+        _ptr(g_saved), act, dgrad_out.data_ptr(), dw2_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _ptr(dev_err), _stream(dev))
+    _check("mc2_gmm_combine_backward", st)
+    return dgrad_out, dw2_out
+
+
+def mc2_gmm_dispatch_backward(dg, recv_counts, send_counts, w1, send_buf, dx_buf, *, ep_rank,
+                              num_experts, world_size_src=1, dw1_out=None, workspace=None,
+                              dev_err=None):
+    """Backward of the grouped fc1: the input gradient goes into the local
+    experts' rows of dx_buf (send-buffer layout); returns (dx_buf, dW1) with
+    dW1 (E_l, H, I2) fp32."""
+    dev = _dev(dg, recv_counts, send_counts, w1, send_buf, dx_buf, dw1_out, workspace, dev_err)
+    E_l, H, I2 = w1.shape
+    if dw1_out is None:
+        dw1_out = torch.empty((E_l, H, I2), dtype=torch.float32, device=dev)
+    need = mc2_gmm_backward_workspace_size(send_buf.shape[0], E_l, H, I2)
+    workspace = _workspace(need, workspace, dev)
+    st = _lib.load().mc2_gmm_dispatch_backward(
+        dg.data_ptr(), dg.shape[0], recv_counts.data_ptr(), send_counts.data_ptr(), world_size_src,
+        ep_rank, num_experts, E_l, w1.data_ptr(), H, I2, send_buf.data_ptr(), send_buf.shape[0],
+        dx_buf.data_ptr(), dx_buf.shape[0], dw1_out.data_ptr(), workspace.data_ptr(),
+        workspace.numel() * workspace.element_size(), _ptr(dev_err), _stream(dev))
+    _check("mc2_gmm_dispatch_backward", st)
+    return dx_buf, dw1_out
+
+
 def mc2_moe_unpermute(y_full, unpermute_idx, probs, *, out=None, dev_err=None):
     dev = _dev(y_full, unpermute_idx, probs, out, dev_err)
     T, K = probs.shape

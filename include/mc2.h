@@ -311,6 +311,54 @@ int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermu
                       const float* probs, int64_t T, int K, int64_t H, void* out,
                       int32_t* dev_err, hipStream_t stream);
 
+/*
+ * Backward of the dispatch / combine pair ["NPU Training Operators - MC2",
+ * "PR 改动": the two autograd Functions wrap the fused operator in forward
+ * and backward; "验证项": fc1 / fc2 gradients are compared with the plain
+ * alltoall path]. Gradients of the forward above, on the local rows:
+ *
+ * mc2_gmm_combine_backward, for each local expert g with rows h_g (of h,
+ * group after group from row 0) and output gradient dY_g (the rows of dy_buf
+ * that mc2_gmm_combine writes for expert ep_rank*E_l + g):
+ *   dA_g  = dY_g @ w2[g]^T                                   (fp32)
+ *   act == MC2_ACT_NONE:   dgrad_out rows = dA_g                 (rows, I) bf16
+ *   act == MC2_ACT_SWIGLU: with the stored fc1 pre-activation g_saved
+ *     (rows, 2I) bf16 = [gate | up], s = 1 / (1 + exp(-gate)):
+ *     dgrad_out rows = [dA*up*s*(1 + gate*(1 - s)) | dA*gate*s]  (rows, 2I) bf16
+ *   dw2_out[g] = h_g^T @ dY_g                               (E_l, I, H) fp32
+ * mc2_gmm_dispatch_backward, with dG_g the rows of dg (group after group
+ * from row 0) and R_g this rank's rows of send_buf:
+ *   dx_buf rows of expert ep_rank*E_l + g = dG_g @ w1[g]^T  (bf16; other rows
+ *   untouched);  dw1_out[g] = R_g^T @ dG_g                   (E_l, H, I2) fp32
+ * Weights as in the forward: w2 (E_l, I, H), w1 (E_l, H, I2), bf16. Counts
+ * and their checks as for mc2_gmm_dispatch (MC2_DEVERR_COUNTS, nothing
+ * computed, on a mismatch or when rows exceed a buffer). An expert with no
+ * rows gets a zero weight gradient. A weight gradient over more than 4096
+ * rows of one expert is split into slices of 4096 rows whose partial tiles are
+ * summed in slice order (the result does not depend on timing). workspace:
+ * caller-owned, 16-byte aligned, at least
+ * mc2_gmm_backward_workspace_size(rows, E_l, M, N) bytes with (rows, M, N) =
+ * (h_rows, I, H) for the combine backward and (send_rows, H, I2) for the
+ * dispatch backward (the rows transposed, each expert padded to 64, tile
+ * counters and partial tiles); no initialisation needed. Constraints: I, H,
+ * I2 multiples of 8.
+ */
+size_t mc2_gmm_backward_workspace_size(int64_t rows, int local_experts, int64_t M, int64_t N);
+
+int mc2_gmm_combine_backward(const void* dy_buf, int64_t dy_rows, const int32_t* recv_counts,
+                             const int32_t* send_counts, int world_size_src, int ep_rank,
+                             int num_experts, int local_experts, const void* w2, int64_t I,
+                             int64_t H, const void* h, int64_t h_rows, const void* g_saved,
+                             int act, void* dgrad_out, float* dw2_out, void* workspace,
+                             size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
+
+int mc2_gmm_dispatch_backward(const void* dg, int64_t dg_rows, const int32_t* recv_counts,
+                              const int32_t* send_counts, int world_size_src, int ep_rank,
+                              int num_experts, int local_experts, const void* w1, int64_t H,
+                              int64_t I2, const void* send_buf, int64_t send_rows, void* dx_buf,
+                              int64_t dx_rows, float* dw1_out, void* workspace, size_t ws_bytes,
+                              int32_t* dev_err, hipStream_t stream);
+
 /* Human-readable name of an mc2_status value (static storage). */
 const char* mc2_status_string(int status);
 

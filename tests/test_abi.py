@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 14, names
+    assert len(names) == 17, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -154,3 +154,28 @@ def test_mm_ar_validates(lib):
     assert g(FAKE, 33, 1024, BF16, 1, FAKE, None) == ERR_SHAPE
     assert g(FAKE, 4, 1020, BF16, 1, FAKE, None) == ERR_ALIGN
     assert g(FAKE, 4, 1024, F32, 1, FAKE, None) == ERR_DTYPE
+
+
+def test_gmm_backward_validates(lib):
+    # transposed rows (each expert padded to 64), counters, no split slots below 2048 rows
+    ws = lib.mc2_gmm_backward_workspace_size(1000, 16, 768, 2048)
+    pt = 768 * ((1000 + 64 * 16 + 63) // 64 * 64) * 2
+    assert ws == (pt + 255) // 256 * 256 + (3 * 8 * 16 * 4 + 255) // 256 * 256
+    big = lib.mc2_gmm_backward_workspace_size(40000, 16, 768, 2048)
+    pt = 768 * ((40000 + 64 * 16 + 63) // 64 * 64) * 2
+    assert big == (pt + 255) // 256 * 256 + 1536 + (2 * 40000 // 4096) * 24 * 256 * 256 * 4
+    assert lib.mc2_gmm_backward_workspace_size(1000, 0, 768, 64) == 0
+    Cb = lib.mc2_gmm_combine_backward
+    base = (FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 128, FAKE, 100)
+    assert Cb(*base, None, 1, FAKE, FAKE, FAKE, 1 << 24, None, None) == ERR_NULL     # SwiGLU needs g_saved
+    assert Cb(*base, None, 0, FAKE, FAKE, None, 0, None, None) == ERR_NULL          # workspace
+    assert Cb(*base, None, 0, FAKE, FAKE, FAKE, 16, None, None) == ERR_WS
+    assert Cb(*base, None, 2, FAKE, FAKE, FAKE, 1 << 24, None, None) == ERR_SHAPE    # unknown act
+    assert Cb(*base[:4], 2, *base[5:], None, 0, FAKE, FAKE, FAKE, 1 << 24, None, None) == ERR_UNSUP
+    assert Cb(*base[:9], 60, *base[10:], None, 0, FAKE, FAKE, FAKE, 1 << 24, None, None) == ERR_ALIGN
+    Db = lib.mc2_gmm_dispatch_backward
+    dbase = (FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 128, FAKE, 100, FAKE, 100, FAKE)
+    assert Db(*dbase, FAKE, 16, None, None) == ERR_WS
+    assert Db(*dbase, FAKE + 8, 1 << 24, None, None) == ERR_ALIGN
+    assert Db(*dbase[:15], None, FAKE, 1 << 24, None, None) == ERR_NULL
+    assert Db(*dbase[:5], 4, *dbase[6:], FAKE, 1 << 24, None, None) == ERR_SHAPE     # ep_rank < E / E_l

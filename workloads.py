@@ -202,6 +202,21 @@ def c4_inputs(seed=1004):
     return moe_inputs(seed)
 
 
+def moe_backward_inputs(seed, rows, hidden, inter, std=1.0):
+    """Stand-ins for the tensors the backward of the MoE local path reads,
+    for `rows` local rows, bf16, all N(0, std). Draw order: dy (rows, H), the
+    output gradient in the combine buffer's rows; g (rows, 2I), the stored fc1
+    pre-activation; h (rows, I), the stored fc2 input; dg (rows, 2I), the fc1
+    output gradient; send (rows, H), the send-buffer rows of the local
+    experts."""
+    rng = np.random.default_rng(seed)
+    return {"dy": _normal(rng, (rows, hidden), std, BF16),
+            "g": _normal(rng, (rows, 2 * inter), std, BF16),
+            "h": _normal(rng, (rows, inter), std, BF16),
+            "dg": _normal(rng, (rows, 2 * inter), std, BF16),
+            "send": _normal(rng, (rows, hidden), std, BF16)}
+
+
 def combine_standins(seed, rows, hidden, std=0.05):
     """Stand-in rows for the part of the combine buffer that other ranks
     would return (N(0, 0.05), bf16)."""
