@@ -211,3 +211,29 @@ def test_weight_gradient_split_groups_deterministic():
     _, ref_dw1 = om.dispatch_backward(b["dg"], recv, send_counts, ep_rank=0, local_experts=3,
                                       w1=d["w1"], send_buf=b["send"], dx_buf=np.zeros((n, H)))
     _assert_wgrad(outs[0][0], ref_dw1, _dec(b["send"]), _dec(b["dg"]), recv, "split dW1")
+
+
+def test_backward_no_local_rows():
+    """Every local expert receives no rows: the weight gradients are exact
+    zeros and no input-gradient row is written."""
+    H, I = 64, 32
+    send_counts = np.array([7, 0, 0, 5], dtype=np.int32)
+    recv = send_counts[1:3].copy()
+    d = wl.moe_inputs(seed=76, tokens=8, hidden=H, num_experts=4, topk=1, local_experts=2,
+                      inter=I)
+    b = wl.moe_backward_inputs(77, 12, H, I)
+    rc, sc = to_dev(recv), to_dev(send_counts)
+    dgrad = torch.full((4, 2 * I), 9.0, dtype=torch.bfloat16, device="cuda")
+    dx = torch.full((12, H), 9.0, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _, dw2 = mc2.mc2_gmm_combine_backward(to_dev(b["dy"], "bf16"), rc, sc, to_dev(d["w2"], "bf16"),
+                                          to_dev(b["h"][:4], "bf16"), ep_rank=1, num_experts=4,
+                                          act=mc2.MC2_ACT_SWIGLU, g_saved=to_dev(b["g"][:4], "bf16"),
+                                          dgrad_out=dgrad, dev_err=err)
+    _, dw1 = mc2.mc2_gmm_dispatch_backward(to_dev(b["dg"][:4], "bf16"), rc, sc,
+                                           to_dev(d["w1"], "bf16"), to_dev(b["send"], "bf16"), dx,
+                                           ep_rank=1, num_experts=4, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert not dw2.any() and not dw1.any()
+    assert (dgrad.float() == 9.0).all() and (dx.float() == 9.0).all()
