@@ -217,8 +217,8 @@ def test_backward_no_local_rows():
     """Every local expert receives no rows: the weight gradients are exact
     zeros and no input-gradient row is written."""
     H, I = 64, 32
-    send_counts = np.array([7, 0, 0, 5], dtype=np.int32)
-    recv = send_counts[1:3].copy()
+    send_counts = np.array([7, 5, 0, 0], dtype=np.int32)  # experts 2, 3 are rank 1's
+    recv = send_counts[2:4].copy()
     d = wl.moe_inputs(seed=76, tokens=8, hidden=H, num_experts=4, topk=1, local_experts=2,
                       inter=I)
     b = wl.moe_backward_inputs(77, 12, H, I)
