@@ -690,8 +690,9 @@ struct WgradArgs {
 // dW[g] = P_g^T @ Q_g (M x N per local group g). Work unit = (group g, K
 // slice s, tile): a 256 x 256 tile over rows [s*L, min((s+1)*L, count g)) of
 // the group, L = kSliceRows; A is the group's column range of the transposed
-// workspace, B the group's rows of Q. Units are numbered group by group,
-// slice by slice, tile fastest. A group of one slice stores its tile; for a
+// workspace, B the group's rows of Q. Units are numbered group by group, the
+// groups with most rows first (so the longest units are dispatched first and
+// the short ones fill the end of the launch), slice by slice, tile fastest. A group of one slice stores its tile; for a
 // split group every slice stores its partial tile in its slot, and the last
 // slice to finish a tile (counted with an agent-scope release / acquire, as
 // the ready flags) sums the partials in slice order, so the result does not
@@ -702,18 +703,27 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   constexpr int kSmem = TS::kStages * TS::kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   __shared__ GroupTable t;
-  __shared__ int64_t s_ustart[kMaxLocalExperts + 1];
-  __shared__ int64_t s_slot[kMaxLocalExperts + 1];
+  __shared__ int64_t s_ustart[kMaxLocalExperts + 1];  // by position in the order
+  __shared__ int64_t s_slot[kMaxLocalExperts + 1];    // by group
+  __shared__ int s_order[kMaxLocalExperts];           // position -> group
   __shared__ int s_last;
   lds_t* smem = (lds_t*)smem_raw;
   load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
   const int El = p.local_experts;
   const int per_group = p.tiles_m * p.tiles_n;
+  for (int e = threadIdx.x; e < El; e += kThreads) {
+    const int32_t c = t.cnt[e];
+    int rank = 0;
+    for (int f = 0; f < El; ++f) rank += t.cnt[f] > c || (t.cnt[f] == c && f < e);
+    s_order[rank] = e;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     int64_t u = 0, slot = 0;
-    for (int e = 0; e < El; ++e) {
+    for (int q = 0; q < El; ++q) {
+      const int e = s_order[q];
       const int64_t ns = t.cnt[e] > kSliceRows ? (t.cnt[e] + kSliceRows - 1) / kSliceRows : 1;
-      s_ustart[e] = u;
+      s_ustart[q] = u;
       s_slot[e] = slot;
       u += ns * per_group;
       slot += ns > 1 ? ns : 0;
@@ -729,16 +739,17 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   }
   const int64_t u = xcd_tile(blockIdx.x, p.round, gridDim.x);
   if (u >= s_ustart[El]) return;
-  int g = 0;
-  while (g + 1 < El && s_ustart[g + 1] <= u) ++g;
-  const int64_t lu = u - s_ustart[g];
+  int q = 0;
+  while (q + 1 < El && s_ustart[q + 1] <= u) ++q;
+  const int g = s_order[q];
+  const int64_t lu = u - s_ustart[q];
   const int s = static_cast<int>(lu / per_group);
   const int lt = static_cast<int>(lu - static_cast<int64_t>(s) * per_group);
   const int tm = lt % p.tiles_m, tn = lt / p.tiles_m;
   const int64_t row0 = static_cast<int64_t>(tm) * TS::BM;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
   const int64_t cnt = t.cnt[g];
-  const int64_t nslices = (s_ustart[g + 1] - s_ustart[g]) / per_group;
+  const int64_t nslices = (s_ustart[q + 1] - s_ustart[q]) / per_group;
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
   if (cnt == 0) {
