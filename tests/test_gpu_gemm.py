@@ -130,6 +130,31 @@ def test_ag_mm_with_flags(rank, x2_trans):
     assert_tol(to_f64(out), ref, "ag_mm")
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F16])
+def test_rs_longest_k_and_most_chunks(dtype):
+    """K = 65528 (the largest multiple of 8 below 65535) over W = 32 chunks of 8
+    rows each, n = 8: one tile per chunk, 1024 K stages, with flags."""
+    W = 32
+    d = wl.gemm_inputs(92, W * 8, 65528, 8, dtype, std=1.0)
+    t = "bf16" if dtype == wl.BF16 else None
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(W, dtype=torch.int32, device="cuda")
+    out = mc2.mc2_mm_rs_local(to_dev(d["x1"], t), to_dev(d["x2"], t), W, 31, ready_flags=flags,
+                              flag_counters=cnt, epoch=6)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [6] * W and cnt.cpu().tolist() == [0] * W
+    assert_tol(to_f64(out), _oracle_rs(d, W), f"k=65528 {dtype}")
+
+
+def test_ag_mm_smallest_shapes():
+    """k = 8 and n = 8 (one 16-byte piece each), one row per chunk."""
+    W = 8
+    d = wl.gemm_inputs(93, W, 8, 8, wl.BF16, std=1.0)
+    out = mc2.mc2_ag_mm_local(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 3)
+    torch.cuda.synchronize()
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "k=n=8")
+
+
 def test_rs_flags_reset_between_calls():
     W = 4
     d = wl.gemm_inputs(27, W * 256, 512, 512, wl.BF16, std=1.0)
