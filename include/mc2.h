@@ -330,7 +330,10 @@ int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermu
  * from row 0) and R_g this rank's rows of send_buf:
  *   dx_buf rows of expert ep_rank*E_l + g = dG_g @ w1[g]^T  (bf16; other rows
  *   untouched);  dw1_out[g] = R_g^T @ dG_g                   (E_l, H, I2) fp32
- * Weights as in the forward: w2 (E_l, I, H), w1 (E_l, H, I2), bf16. Counts
+ * Buffers: dy_buf (dy_rows, H); h (h_rows, I); g_saved (h_rows, 2I) or NULL
+ * with MC2_ACT_NONE; dgrad_out (h_rows, I or 2I); dg (dg_rows, I2); send_buf
+ * and dx_buf (send_rows / dx_rows, H); all bf16, rows packed. Weights as in
+ * the forward: w2 (E_l, I, H), w1 (E_l, H, I2), bf16. Counts
  * and their checks as for mc2_gmm_dispatch (MC2_DEVERR_COUNTS, nothing
  * computed, on a mismatch or when rows exceed a buffer). An expert with no
  * rows gets a zero weight gradient. A weight gradient over more than 4096
