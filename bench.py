@@ -35,9 +35,12 @@ PEAK_HBM = 8000.0    # GB/s, HBM3E (published)
 
 # Sources of the headline kernel: the HBM traffic recorded under profiles/ is
 # reported only while these files are unchanged since the counters were taken.
+# the sources of the headline kernel (the grouped and MoE kernels live elsewhere)
 KERNEL_SOURCES = ["gemm_collective_core_amd/csrc/gemm_core.hpp",
+                  "gemm_collective_core_amd/csrc/mc2_tiles.hpp",
                   "gemm_collective_core_amd/csrc/mc2_gemm.hip",
-                  "gemm_collective_core_amd/csrc/mc2_common.hpp"]
+                  "gemm_collective_core_amd/csrc/mc2_common.hpp",
+                  "gemm_collective_core_amd/csrc/mc2_host.hpp"]
 TRAFFIC_FILE = "profiles/traffic_ag_mm_bf16_8192x3072x3072.json"
 
 

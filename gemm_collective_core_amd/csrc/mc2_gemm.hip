@@ -1,107 +1,12 @@
 // Rank-chunked GEMM (MatmulReduceScatter / AllGatherMatmul compute share) and
-// the grouped GEMM of the MoE dispatch/combine pair, for gfx950.
+// the MatmulAllReduce local share, for gfx950.
 //
 // Formulas: torch_npu.npu_mm_reduce_scatter_base API doc, "功能说明" (basic and
 // quantized MatmulReduceScatter); CANN hccl issue 158 (AllGatherMatmul);
-// "NPU Training Operators - MC2", "执行路径" (GroupedMatmul fc1 + swiglu, fc2).
-#include "../../include/mc2.h"
-#include "gemm_core.hpp"
-#include "mc2_host.hpp"
+// "NPU Training Operators - MC2", "底层 API 对照" (MatmulAllReduce).
+#include "mc2_tiles.hpp"
 
 namespace mc2 {
-
-// ---------------------------------------------------------------- epilogues
-
-template <Out O>
-__device__ __forceinline__ void put_out(lds_t* p, float v) {
-  if constexpr (O == Out::BF16) *reinterpret_cast<MC2_LDS uint16_t*>(p) = f32_to_bf16_bits(v);
-  else if constexpr (O == Out::F16) *reinterpret_cast<MC2_LDS uint16_t*>(p) = f32_to_f16_bits(v);
-  else *reinterpret_cast<MC2_LDS float*>(p) = v;
-}
-
-template <Out O, class V>
-__device__ __forceinline__ void put_out_global(char* p, V v) {
-  if constexpr (O == Out::I32) *reinterpret_cast<int32_t*>(p) = v;
-  else *reinterpret_cast<float*>(p) = v;
-}
-
-template <Elem E>
-__device__ __forceinline__ float load_bias(const void* bias, int64_t j) {
-  const uint16_t b = static_cast<const uint16_t*>(bias)[j];
-  if constexpr (E == Elem::F16) return f16_bits_to_f32(b);
-  else return bf16_bits_to_f32(b);  // BF16 inputs, and the bf16 bias of int8 inputs
-}
-
-// Elementwise epilogue of the linear kernels: for every accumulator element
-// of the wave, computes the output value and hands it with its tile-local row
-// and column to `sink`.
-//   16-bit inputs: acc + bias_mul * bias[j]  (bias_mul = number of partials)
-//   int8 inputs:   (x1_scale[i] * x2_scale[j]) * (float(acc) + bias[j]),
-//                  or the raw accumulator for 32-bit integer output
-template <Elem E, class TS, Out O, class Sink>
-__device__ __forceinline__ void epilogue_linear(const typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN],
-                                                int64_t row0, int64_t row_last, int64_t col0,
-                                                int64_t n, const void* bias, float bias_mul,
-                                                const float* s1, const float* s2, Sink&& sink) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow0 = (wave / TS::WN) * TS::WTM;
-  const int wcol0 = (wave % TS::WN) * TS::WTN;
-#pragma unroll
-  for (int fn = 0; fn < TS::FN; ++fn) {
-    const int lcol = wcol0 + fn * 16 + (lane & 15);
-    int64_t gcol = col0 + lcol;
-    gcol = gcol < n ? gcol : n - 1;
-    float bv = 0.f;
-    if (bias) bv = load_bias<E>(bias, gcol);
-    float sc2 = 1.f;
-    if constexpr (E == Elem::I8 && O != Out::I32) sc2 = s2[gcol];
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
-        if constexpr (E == Elem::I8) {
-          if constexpr (O == Out::I32) {
-            sink(lrow, lcol, acc[fm][fn][i]);
-          } else {
-            int64_t grow = row0 + lrow;
-            grow = grow < row_last ? grow : row_last;
-            const float sc = s1[grow] * sc2;
-            sink(lrow, lcol, sc * (static_cast<float>(acc[fm][fn][i]) + bv));
-          }
-        } else {
-          sink(lrow, lcol, acc[fm][fn][i] + bias_mul * bv);
-        }
-      }
-    }
-  }
-}
-
-// SwiGLU epilogue: tile column blocks alternate gate (even) and up (odd), so
-// the fragments fn = 2p and 2p + 1 of a lane hold gate and up of the same
-// output column. h = silu(g) * u, silu(g) = g / (1 + exp(-g)), stored as bf16.
-template <class TS>
-__device__ __forceinline__ void stage_swiglu(lds_t* smem, int pitch,
-                                             const f32x4_t (&acc)[TS::FM][TS::FN]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow0 = (wave / TS::WN) * TS::WTM;
-  const int wcol0 = (wave % TS::WN) * TS::WTN;
-#pragma unroll
-  for (int p = 0; p < TS::FN / 2; ++p) {
-    const int lcol = wcol0 / 2 + p * 16 + (lane & 15);
-#pragma unroll
-    for (int fm = 0; fm < TS::FM; ++fm) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
-        const float g = acc[fm][2 * p][i];
-        const float u = acc[fm][2 * p + 1][i];
-        const float h = g / (1.0f + __expf(-g)) * u;
-        *reinterpret_cast<MC2_LDS uint16_t*>(smem + lrow * pitch + lcol * 2) = f32_to_bf16_bits(h);
-      }
-    }
-  }
-}
 
 // ---------------------------------------------------------------- chunked GEMM
 
@@ -155,32 +60,12 @@ __device__ __forceinline__ void wait_input_segment(const ChunkedArgs& p, int g) 
   __syncthreads();
 }
 
-// Tile column -> global column of B, clamped to the last 16-byte column block.
-struct PlainCols {
-  int64_t col0, last_block;
-  __device__ __forceinline__ int64_t operator()(int j) const {
-    const int64_t c = col0 + j;
-    return c < last_block ? c : last_block;
-  }
-};
-
 template <class TS, int OS>
 constexpr int chunked_smem() {
   // 32-bit outputs are not staged through LDS
   return (OS == 4 || TS::kStages * TS::kStageBytes > TS::BM * (TS::BN * OS + 16))
              ? TS::kStages * TS::kStageBytes
              : TS::BM * (TS::BN * OS + 16);
-}
-
-// Logical tile of workgroup b. Workgroups are dispatched to the 8 XCDs in
-// turn (b mod 8), each XCD with its own L2. Inside every round of `round`
-// workgroups (one per CU), XCD x is given the round's logical tiles
-// 32x .. 32x+31 (round/8 of them): consecutive tiles, which share rows of A
-// and columns of B, then run on the same L2.
-__device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
-  if (round <= 0 || b >= (nblocks / round) * round) return b;
-  const int r = b / round, u = b - r * round;
-  return r * round + (u & 7) * (round >> 3) + (u >> 3);
 }
 
 // One output tile (or the row half `half` of one, for a TS of half height):
@@ -291,528 +176,6 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
   chunked_tile<E, BT, TS, O>(p, smem, u, 0, 2u);
 }
 
-// ---------------------------------------------------------------- grouped GEMM
-
-constexpr int kMaxLocalExperts = 256;
-
-struct GroupedArgs {
-  const char* A;
-  int64_t lda;
-  const char* B;
-  int64_t ldb, b_group;   // bytes per B row, bytes per expert
-  char* out;
-  int64_t ldo;
-  int64_t K;              // contraction length
-  int64_t n_b;            // columns of B per expert
-  int64_t n_out;          // output columns
-  int64_t inter;          // SwiGLU: output columns (= n_b / 2)
-  const int32_t* send_counts;
-  const int32_t* recv_counts;
-  int ep_rank, num_experts, local_experts;
-  int combine;            // 0: rows read at the send offset; 1: rows written there
-  int64_t a_cap, o_cap;   // row capacities of the A and output buffers
-  int32_t* dev_err;
-  int ktiles;
-  const char* gsave;      // SwiGLU backward: the fc1 pre-activation (rows, 2*inter) bf16
-  int64_t ldg;            // bytes per gsave row
-};
-
-// Epilogue of the grouped kernel.
-enum GroupedMode : int {
-  kLinear = 0,   // out = acc (bf16)
-  kSwiglu = 1,   // out = silu(gate) * up of the interleaved gate / up columns
-  kSwigluBwd = 2 // acc = gradient of the SwiGLU output; out = gradient of its input
-};
-
-struct GluCols {
-  // Tile column j (16-column blocks alternate gate / up) -> global B column,
-  // clamped to the last 16-byte block; clamped columns only feed output
-  // columns >= inter, which are never stored.
-  int64_t j0, inter, last_block;
-  __device__ __forceinline__ int64_t operator()(int j) const {
-    const int cb = j >> 4;
-    const int64_t base = (cb & 1) ? inter : 0;
-    const int64_t c = base + j0 + (cb >> 1) * 16 + (j & 15);
-    return c < last_block ? c : last_block;
-  }
-};
-
-template <class TS, int MODE>
-constexpr int grouped_smem() {
-  // kSwigluBwd stages fp32 values, half a tile's rows at a time
-  constexpr int stage = MODE == kSwigluBwd ? (TS::BM / 2) * (TS::BN * 4 + 16)
-                                           : TS::BM * ((MODE == kSwiglu ? TS::BN / 2 : TS::BN) * 2 + 16);
-  return TS::kStages * TS::kStageBytes > stage ? TS::kStages * TS::kStageBytes : stage;
-}
-
-// SwiGLU backward epilogue: the accumulator holds dA, the gradient of the
-// SwiGLU output, for output rows [orow0, orow0 + nrows) and columns
-// [ocol0, ocol0 + BN) of the inter columns. With the stored pre-activation
-// (gate in columns [0, inter), up in [inter, 2 inter)):
-//   d_gate = dA * up * s * (1 + gate * (1 - s)),  d_up = dA * gate * s,
-//   s = 1 / (1 + exp(-gate)),
-// written as bf16 to the same columns of `out`. dA goes through LDS in fp32,
-// half the tile's rows at a time, so that every thread then handles 8
-// consecutive columns with 16-byte loads and stores.
-template <class TS>
-__device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (&acc)[TS::FM][TS::FN],
-                                                    const GroupedArgs& p, int64_t orow0,
-                                                    int64_t nrows, int64_t ocol0) {
-  constexpr int HR = TS::BM / 2;
-  constexpr int pitch = TS::BN * 4 + 16;
-  constexpr int CPR = TS::BN / 8;  // 8-column pieces per row
-  static_assert(TS::WTM == HR, "each wave's rows must lie in one half");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wrow0 = (wave / TS::WN) * TS::WTM;
-  const int wcol0 = (wave % TS::WN) * TS::WTN;
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();
-    if (wrow0 == half * HR) {
-#pragma unroll
-      for (int fn = 0; fn < TS::FN; ++fn) {
-        const int lcol = wcol0 + fn * 16 + (lane & 15);
-#pragma unroll
-        for (int fm = 0; fm < TS::FM; ++fm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int lrow = fm * 16 + 4 * (lane >> 4) + i;
-            *reinterpret_cast<MC2_LDS float*>(smem + lrow * pitch + lcol * 4) = acc[fm][fn][i];
-          }
-      }
-    }
-    __syncthreads();
-    for (int q = tid; q < HR * CPR; q += kThreads) {
-      const int r = q / CPR, c8 = q - r * CPR;
-      const int64_t row = half * HR + r;
-      const int64_t col = ocol0 + c8 * 8;
-      if (row >= nrows || col >= p.inter) continue;
-      const MC2_LDS float* src = reinterpret_cast<const MC2_LDS float*>(smem + r * pitch + c8 * 32);
-      const char* grow = p.gsave + (orow0 + row) * p.ldg;
-      const u32x4_t gv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(grow + col * 2));
-      const u32x4_t uv =
-          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(grow + (p.inter + col) * 2));
-      u32x4_t dg, du;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t lo_g = 0, lo_u = 0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const float da = src[2 * j + h];
-          const float g = bf16_bits_to_f32((gv[j] >> (16 * h)) & 0xFFFFu);
-          const float u = bf16_bits_to_f32((uv[j] >> (16 * h)) & 0xFFFFu);
-          const float sg = 1.0f / (1.0f + __expf(-g));
-          lo_g |= static_cast<uint32_t>(f32_to_bf16_bits(da * u * (sg * (1.0f + g * (1.0f - sg)))))
-                  << (16 * h);
-          lo_u |= static_cast<uint32_t>(f32_to_bf16_bits(da * (g * sg))) << (16 * h);
-        }
-        dg[j] = lo_g;
-        du[j] = lo_u;
-      }
-      char* orow = p.out + (orow0 + row) * p.ldo;
-      __builtin_nontemporal_store(dg, reinterpret_cast<u32x4_t*>(orow + col * 2));
-      __builtin_nontemporal_store(du, reinterpret_cast<u32x4_t*>(orow + (p.inter + col) * 2));
-    }
-  }
-}
-
-// Persistent grouped GEMM: every workgroup derives the tile -> (expert, rows,
-// columns) map from the device-side counts, so the host never reads them.
-template <class TS, int MODE, bool BT>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
-  constexpr bool GLU = MODE == kSwiglu;
-  static_assert(!(GLU && BT), "the interleaved gate / up columns need row-major weights");
-  constexpr int kSmem = grouped_smem<TS, MODE>();
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
-  lds_t* smem = (lds_t*)smem_raw;
-  __shared__ int64_t s_gstart[kMaxLocalExperts + 1];
-  __shared__ int64_t s_tstart[kMaxLocalExperts + 1];
-  __shared__ int64_t s_base;
-  __shared__ int s_bad;
-
-  const int tid = threadIdx.x;
-  const int El = p.local_experts;
-  const int first = p.ep_rank * El;
-  constexpr int OUTC = GLU ? TS::BN / 2 : TS::BN;  // output columns per tile
-  const int64_t tiles_n = (p.n_out + OUTC - 1) / OUTC;
-
-  // Counts -> group table.
-  if (tid == 0) { s_base = 0; s_bad = 0; }
-  __syncthreads();
-  int64_t part = 0;
-  for (int e = tid; e < first; e += kThreads) {
-    const int32_t v = p.send_counts[e];
-    if (v < 0) s_bad = 1;
-    part += v;
-  }
-  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-  if ((tid & 63) == 0 && part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_base),
-                                         static_cast<unsigned long long>(part));
-  if (tid == 0) {
-    int64_t g = 0, tt = 0;
-    for (int e = 0; e < El; ++e) {
-      const int32_t rc = p.recv_counts[e];
-      if (rc < 0 || rc != p.send_counts[first + e]) s_bad = 1;
-      s_gstart[e] = g;
-      s_tstart[e] = tt;
-      g += rc > 0 ? rc : 0;
-      tt += ((rc > 0 ? rc : 0) + TS::BM - 1) / TS::BM * tiles_n;
-    }
-    s_gstart[El] = g;
-    s_tstart[El] = tt;
-  }
-  __syncthreads();
-  {
-    const int64_t rows = s_gstart[El];
-    const int64_t a_need = (p.combine ? 0 : s_base) + rows;
-    const int64_t o_need = (p.combine ? s_base : 0) + rows;
-    if (s_bad || a_need > p.a_cap || o_need > p.o_cap) {
-      if (tid == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
-      return;
-    }
-  }
-  const int64_t a_base = p.combine ? 0 : s_base;
-  const int64_t o_base = p.combine ? s_base : 0;
-  const int64_t total = s_tstart[El];
-
-  KSpan ks{p.K, 0, 0, p.ktiles, p.ktiles};
-  // With one workgroup per CU (a multiple of 8), XCD x takes tiles 32x ..
-  // 32x+31 of every round of the tile sequence (see xcd_tile).
-  const int g8 = gridDim.x;
-  const int64_t tfirst = (g8 % 8 == 0) ? (blockIdx.x & 7) * (g8 >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  for (int64_t t = tfirst; t < total; t += gridDim.x) {
-    int g = 0;
-    while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
-    const int64_t cnt = s_gstart[g + 1] - s_gstart[g];
-    const int64_t tiles_m = (cnt + TS::BM - 1) / TS::BM;
-    const int64_t lt = t - s_tstart[g];
-    const int64_t tm = lt % tiles_m, tn = lt / tiles_m;
-    const int64_t arow0 = a_base + s_gstart[g] + tm * TS::BM;
-    const int64_t arow_end = a_base + s_gstart[g] + cnt;
-    const int64_t orow0 = o_base + s_gstart[g] + tm * TS::BM;
-    const int64_t ocol0 = tn * OUTC;
-
-    f32x4_t acc[TS::FM][TS::FN];
-    BDesc bd{p.B + g * p.b_group, p.ldb, p.n_b};
-    if constexpr (GLU) {
-      GluCols cm{ocol0, p.inter, p.n_b - 8};
-      mainloop<Elem::BF16, false, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
-    } else {
-      PlainCols cm{ocol0, p.n_b - 8};
-      mainloop<Elem::BF16, BT, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks, acc);
-    }
-    if constexpr (MODE == kSwigluBwd) {
-      swiglu_bwd_epilogue<TS>(smem, acc, p, orow0, arow_end - arow0, ocol0);
-      __syncthreads();
-      continue;
-    }
-    constexpr int pitch = OUTC * 2 + 16;
-    if constexpr (GLU)
-      stage_swiglu<TS>(smem, pitch, acc);
-    else
-      epilogue_linear<Elem::BF16, TS, Out::BF16>(
-          acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
-          [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
-    __syncthreads();
-    store_staged(smem, pitch, OUTC * 2, TS::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
-                 ocol0 * 2, p.n_out * 2);
-    __syncthreads();
-  }
-}
-
-// ---------------------------------------------------------------- weight gradients
-
-// Group table of the local experts from the device-side counts, in shared
-// memory: row starts (gstart), starts of each group's columns in the
-// transposed workspace (pstart: group sizes rounded up to 64, so that every
-// 64-element K stage of a group is one aligned 128-byte line), and the
-// send-buffer row of local expert 0 (base). bad is set when the counts are
-// negative or recv_counts disagree with the send counts of this rank's
-// experts. The counts are read by many threads at once; one thread then sums
-// them in shared memory.
-constexpr int kGroupAlign = 64;
-
-struct GroupTable {
-  int64_t gstart[kMaxLocalExperts + 1];
-  int64_t pstart[kMaxLocalExperts + 1];
-  int32_t cnt[kMaxLocalExperts];
-  int64_t base;
-  int bad;
-};
-
-__device__ __forceinline__ void load_group_table(GroupTable& t, const int32_t* send_counts,
-                                                 const int32_t* recv_counts, int ep_rank, int El) {
-  const int tid = threadIdx.x;
-  const int first = ep_rank * El;
-  if (tid == 0) { t.base = 0; t.bad = 0; }
-  __syncthreads();
-  int64_t part = 0;
-  for (int e = tid; e < first; e += blockDim.x) {
-    const int32_t v = send_counts[e];
-    if (v < 0) t.bad = 1;
-    part += v;
-  }
-  for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
-  if ((tid & 63) == 0 && part) atomicAdd(reinterpret_cast<unsigned long long*>(&t.base),
-                                         static_cast<unsigned long long>(part));
-  for (int e = tid; e < El; e += blockDim.x) {
-    const int32_t rc = recv_counts[e];
-    if (rc < 0 || rc != send_counts[first + e]) t.bad = 1;
-    t.cnt[e] = rc > 0 ? rc : 0;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int64_t g = 0, q = 0;
-    for (int e = 0; e < El; ++e) {
-      const int64_t c = t.cnt[e];
-      t.gstart[e] = g;
-      t.pstart[e] = q;
-      g += c;
-      q += (c + kGroupAlign - 1) & ~int64_t{kGroupAlign - 1};
-    }
-    t.gstart[El] = g;
-    t.pstart[El] = q;
-  }
-  __syncthreads();
-}
-
-struct TransposeArgs {
-  const char* P;      // rows (ld bytes each); this rank's rows start at row base (at_send) or 0
-  int64_t ldp;
-  int at_send;
-  int64_t cols;       // C, multiple of 8
-  int64_t p_cap;      // rows of P
-  char* PT;           // (C, kt) bf16
-  int64_t kt;         // elements per PT row
-  const int32_t* send_counts;
-  const int32_t* recv_counts;
-  int ep_rank, local_experts;
-  int32_t* dev_err;
-  uint32_t* zero;     // n_zero words cleared by workgroup (0, 0): the weight-gradient counters
-  int64_t n_zero;
-};
-
-// PT[c][pstart[g] + i] = P[base + gstart[g] + i][c] for every local group g
-// and row i < count g; the up-to-7 columns after each group are zeroed, so
-// that a 16-byte K piece read past the group's last row holds zeros. One
-// workgroup takes 64 rows and walks over the columns in 64-column blocks,
-// each through LDS: 16-byte loads along the rows, then each wave writes 64
-// consecutive columns of one PT row.
-__global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
-  __shared__ GroupTable t;
-  constexpr int pitch = 132;  // bytes per LDS row: 64 bf16 + 4, so a column read is conflict-free
-  __shared__ __attribute__((aligned(16))) char tile_raw[64 * pitch];
-  __shared__ int64_t s_dcol[64];
-  lds_t* tile = (lds_t*)tile_raw;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
-    for (int64_t i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero[i] = 0u;
-  load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
-  const int El = p.local_experts;
-  const int64_t n = t.gstart[El];
-  const int64_t base = p.at_send ? t.base : 0;
-  if (t.bad || base + n > p.p_cap || t.pstart[El] > p.kt) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
-    return;
-  }
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
-  if (r0 >= n) return;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int64_t r = r0 + tid;
-    int g = 0;
-    while (g + 1 < El && t.gstart[g + 1] <= r) ++g;
-    s_dcol[tid] = r < n ? t.pstart[g] + (r - t.gstart[g]) : -1;
-  }
-  __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t dcol = s_dcol[lane];
-  for (int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64; c0 < p.cols; c0 += 64 * gridDim.y) {
-    {
-      const int r = tid >> 3, ch = tid & 7;
-      const int64_t gr = r0 + r, gc = c0 + ch * 8;
-      u32x4_t v = zero_v4();
-      if (gr < n && gc < p.cols)
-        v = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(p.P + (base + gr) * p.ldp + gc * 2));
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<MC2_LDS uint32_t*>(tile + r * pitch + ch * 16 + j * 4) = v[j];
-    }
-    __syncthreads();
-    for (int k = 0; k < 8; ++k) {
-      const int c = wave * 8 + k;
-      if (c0 + c >= p.cols) break;
-      if (dcol >= 0)
-        *reinterpret_cast<uint16_t*>(p.PT + (c0 + c) * p.kt * 2 + dcol * 2) =
-            *reinterpret_cast<const MC2_LDS uint16_t*>(tile + lane * pitch + c * 2);
-    }
-    // zero the padding after every group whose last row lies in this block
-    for (int g = 0; g < El; ++g) {
-      const int64_t last = t.gstart[g + 1] - 1;
-      if (t.gstart[g + 1] == t.gstart[g] || last < r0 || last >= r0 + 64) continue;
-      const int64_t pad0 = t.pstart[g] + (t.gstart[g + 1] - t.gstart[g]);
-      const int64_t pad1 = (pad0 + 7) & ~int64_t{7};
-      const int npad = static_cast<int>(pad1 - pad0);
-      for (int q = tid; q < 64 * 8; q += blockDim.x) {
-        const int c = q >> 3, j = q & 7;
-        if (j < npad && c0 + c < p.cols)
-          *reinterpret_cast<uint16_t*>(p.PT + (c0 + c) * p.kt * 2 + (pad0 + j) * 2) = 0;
-      }
-    }
-    __syncthreads();
-  }
-}
-
-// Rows of one K slice of a weight-gradient tile: a group with more rows is
-// split into slices whose partial tiles are summed afterwards, so that one
-// large group does not set the length of the whole launch.
-constexpr int64_t kSliceRows = 4096;
-
-struct WgradArgs {
-  const char* PT;     // (M, kt) bf16: the transposed group rows
-  int64_t ldpt;       // bytes per PT row
-  const char* Q;      // (rows, N) bf16, this rank's rows from row base (at_send) or 0
-  int64_t ldq;
-  int at_send;
-  int64_t q_cap;
-  float* out;         // (E_l, M, N) fp32
-  int64_t M, N;
-  int tiles_m, tiles_n;
-  int round;
-  uint32_t* counters; // E_l * tiles_m * tiles_n, zero on entry (left zero)
-  float* partials;    // max_slots slices' partial tiles of split groups
-  int64_t max_slots;
-  const int32_t* send_counts;
-  const int32_t* recv_counts;
-  int ep_rank, local_experts;
-  int32_t* dev_err;
-};
-
-// dW[g] = P_g^T @ Q_g (M x N per local group g). Work unit = (group g, K
-// slice s, tile): a 256 x 256 tile over rows [s*L, min((s+1)*L, count g)) of
-// the group, L = kSliceRows; A is the group's column range of the transposed
-// workspace, B the group's rows of Q. Units are numbered group by group, the
-// groups with most rows first (so the longest units are dispatched first and
-// the short ones fill the end of the launch), slice by slice, tile fastest. A group of one slice stores its tile; for a
-// split group every slice stores its partial tile in its slot, and the last
-// slice to finish a tile (counted with an agent-scope release / acquire, as
-// the ready flags) sums the partials in slice order, so the result does not
-// depend on timing. An empty group gets zeros. The grid may have more
-// workgroups than units (the host knows only a bound); the rest exit.
-template <class TS>
-__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
-  constexpr int kSmem = TS::kStages * TS::kStageBytes;
-  __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
-  __shared__ GroupTable t;
-  __shared__ int64_t s_ustart[kMaxLocalExperts + 1];  // by position in the order
-  __shared__ int64_t s_slot[kMaxLocalExperts + 1];    // by group
-  __shared__ int s_order[kMaxLocalExperts];           // position -> group
-  __shared__ int s_last;
-  lds_t* smem = (lds_t*)smem_raw;
-  load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
-  const int El = p.local_experts;
-  const int per_group = p.tiles_m * p.tiles_n;
-  for (int e = threadIdx.x; e < El; e += kThreads) {
-    const int32_t c = t.cnt[e];
-    int rank = 0;
-    for (int f = 0; f < El; ++f) rank += t.cnt[f] > c || (t.cnt[f] == c && f < e);
-    s_order[rank] = e;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int64_t u = 0, slot = 0;
-    for (int q = 0; q < El; ++q) {
-      const int e = s_order[q];
-      const int64_t ns = t.cnt[e] > kSliceRows ? (t.cnt[e] + kSliceRows - 1) / kSliceRows : 1;
-      s_ustart[q] = u;
-      s_slot[e] = slot;
-      u += ns * per_group;
-      slot += ns > 1 ? ns : 0;
-    }
-    s_ustart[El] = u;
-    s_slot[El] = slot;
-  }
-  __syncthreads();
-  const int64_t base = p.at_send ? t.base : 0;
-  if (t.bad || base + t.gstart[El] > p.q_cap || s_slot[El] > p.max_slots) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
-    return;
-  }
-  const int64_t u = xcd_tile(blockIdx.x, p.round, gridDim.x);
-  if (u >= s_ustart[El]) return;
-  int q = 0;
-  while (q + 1 < El && s_ustart[q + 1] <= u) ++q;
-  const int g = s_order[q];
-  const int64_t lu = u - s_ustart[q];
-  const int s = static_cast<int>(lu / per_group);
-  const int lt = static_cast<int>(lu - static_cast<int64_t>(s) * per_group);
-  const int tm = lt % p.tiles_m, tn = lt / p.tiles_m;
-  const int64_t row0 = static_cast<int64_t>(tm) * TS::BM;
-  const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
-  const int64_t cnt = t.cnt[g];
-  const int64_t nslices = (s_ustart[q + 1] - s_ustart[q]) / per_group;
-  float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
-  const int64_t nrows = p.M - row0, ncols = p.N - col0;
-  if (cnt == 0) {
-    for (int q = threadIdx.x; q < TS::BM * TS::BN; q += kThreads) {
-      const int r = q / TS::BN, c = q - r * TS::BN;
-      if (r < nrows && c < ncols) dst[(row0 + r) * p.N + col0 + c] = 0.0f;
-    }
-    return;
-  }
-  const int64_t k0 = static_cast<int64_t>(s) * kSliceRows;
-  const int64_t klen = cnt - k0 < kSliceRows ? cnt - k0 : kSliceRows;
-  const int ktiles = static_cast<int>((klen + 63) / 64);
-  KSpan ks{klen, 0, 0, ktiles, ktiles};
-  f32x4_t acc[TS::FM][TS::FN];
-  BDesc bd{p.Q + (base + t.gstart[g] + k0) * p.ldq, p.ldq, p.N};
-  PlainCols cm{col0, p.N - 8};
-  mainloop<Elem::BF16, false, TS>(smem, p.PT + (t.pstart[g] + k0) * 2, p.ldpt, row0, p.M - 1, bd,
-                                  col0, cm, ks, acc);
-  if (nslices == 1) {
-    char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
-    epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                              nullptr, [&](int r, int c, float v) {
-                                                if (r < nrows && c < ncols)
-                                                  put_out_global<Out::F32>(base_out + (r * p.N + c) * 4, v);
-                                              });
-    return;
-  }
-  // split group: this slice's partial tile (dense BM x BN) into its slot
-  constexpr int64_t kTileElems = static_cast<int64_t>(TS::BM) * TS::BN;
-  float* part0 = p.partials + (s_slot[g] * per_group + lt) * kTileElems;
-  const int64_t slice_stride = per_group * kTileElems;
-  char* mine = reinterpret_cast<char*>(part0 + s * slice_stride);
-  epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                            nullptr, [&](int r, int c, float v) {
-                                              put_out_global<Out::F32>(mine + (r * TS::BN + c) * 4, v);
-                                            });
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  uint32_t* ctr = p.counters + static_cast<int64_t>(g) * per_group + lt;
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const uint32_t prev = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_last = prev + 1 == static_cast<uint32_t>(nslices);
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int q = threadIdx.x; q < TS::BM * TS::BN / 4; q += kThreads) {
-    const int r = q / (TS::BN / 4), c = (q - r * (TS::BN / 4)) * 4;
-    if (r >= nrows || c >= ncols) continue;
-    float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int64_t j = 0; j < nslices; ++j) {
-      const float4 v = *reinterpret_cast<const float4*>(part0 + j * slice_stride + r * TS::BN + c);
-      sum.x += v.x;
-      sum.y += v.y;
-      sum.z += v.z;
-      sum.w += v.w;
-    }
-    *reinterpret_cast<float4*>(dst + (row0 + r) * p.N + col0 + c) = sum;
-  }
-  if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // ---------------------------------------------------------------- all-reduce sum
 
 // fp64 -> fp32 with rounding to odd (truncate; set the last bit when anything
@@ -908,8 +271,6 @@ __global__ __launch_bounds__(256) void ar_sum_kernel(const uint16_t* __restrict_
 
 // ---------------------------------------------------------------- host side
 
-using TileL = Tile<256, 256, 2, 4>;  // wave sub-tile 128 x 64
-using TileM = Tile<128, 256, 2, 4>;  // wave sub-tile 64 x 64, for small tile counts
 
 template <Elem E, bool BT, class TS, Out O>
 static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s) {
@@ -1039,14 +400,6 @@ static int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int
     e = x2_trans ? dispatch_chunked<true, TileM>(in_dtype, out_dtype, a, (int)blocks, stream)
                  : dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
   return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
-}
-
-static bool valid_world(int W) { return W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32; }
-
-// Per-lane buffer offsets are 32-bit: rows of up to 256 (A, B given as (n, k))
-// or 128 (row-major B) per tile must stay below 2^31 bytes.
-static bool offsets_fit(int64_t lda, int64_t ldb) {
-  return lda * 256 < 0x7fff0000LL && ldb * 256 < 0x7fff0000LL;
 }
 
 }  // namespace mc2
@@ -1220,332 +573,4 @@ extern "C" int mc2_mm_ar_local(const void* x1, const void* x2, int64_t m, int64_
     if (st) return st;
   }
   return launch_ar_sum(workspace, W, m * n, in_dtype, rounding, out, stream);
-}
-
-// ---------------------------------------------------------------- grouped entry points
-
-namespace mc2 {
-
-using TileG = TileL;
-
-template <int MODE, bool BT>
-static int run_grouped(const GroupedArgs& a, int64_t max_tiles, hipStream_t stream) {
-  const int64_t grid64 = max_tiles < num_cus() ? max_tiles : num_cus();
-  const int grid = static_cast<int>(grid64 > 0 ? grid64 : 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<TileG, MODE, BT>), dim3(grid), dim3(kThreads), 0, stream,
-                     a);
-  return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
-}
-
-static int check_ep(int world_size_src, int ep_rank, int num_experts, int local_experts) {
-  if (world_size_src != 1) return MC2_ERR_UNSUPPORTED;
-  if (num_experts < 1 || local_experts < 1 || local_experts > kMaxLocalExperts) return MC2_ERR_SHAPE;
-  if (num_experts % local_experts) return MC2_ERR_SHAPE;
-  if (ep_rank < 0 || ep_rank >= num_experts / local_experts) return MC2_ERR_SHAPE;
-  return MC2_OK;
-}
-
-}  // namespace mc2
-
-extern "C" int mc2_gmm_dispatch(const void* send_buf, int64_t send_rows, const int32_t* send_counts,
-                                const int32_t* recv_counts, int world_size_src, int ep_rank,
-                                int num_experts, int local_experts, const void* w1, int64_t H,
-                                int64_t I2, int act, void* h_out, int64_t h_rows,
-                                int32_t* dev_err, hipStream_t stream) {
-  if (!send_buf || !send_counts || !recv_counts || !w1 || !h_out) return MC2_ERR_NULL;
-  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
-  if (st) return st;
-  if (H < 1 || I2 < 16 || send_rows < 0 || h_rows < 0) return MC2_ERR_SHAPE;
-  if (act != MC2_ACT_NONE && act != MC2_ACT_SWIGLU) return MC2_ERR_SHAPE;
-  if (H % 8 || I2 % 16) return MC2_ERR_ALIGN;
-  if (!aligned16(send_buf) || !aligned16(w1) || !aligned16(h_out)) return MC2_ERR_ALIGN;
-  if (!offsets_fit(H * 2, I2 * 2)) return MC2_ERR_UNSUPPORTED;
-  const bool glu = act == MC2_ACT_SWIGLU;
-  GroupedArgs a{};
-  a.A = static_cast<const char*>(send_buf);
-  a.lda = H * 2;
-  a.B = static_cast<const char*>(w1);
-  a.ldb = I2 * 2;
-  a.b_group = H * I2 * 2;
-  a.out = static_cast<char*>(h_out);
-  a.n_b = I2;
-  a.n_out = glu ? I2 / 2 : I2;
-  a.inter = I2 / 2;
-  a.ldo = a.n_out * 2;
-  a.K = H;
-  a.send_counts = send_counts;
-  a.recv_counts = recv_counts;
-  a.ep_rank = ep_rank;
-  a.num_experts = num_experts;
-  a.local_experts = local_experts;
-  a.combine = 0;
-  a.a_cap = send_rows;
-  a.o_cap = h_rows;
-  a.dev_err = dev_err;
-  a.ktiles = static_cast<int>((H + 63) / 64);
-  const int outc = glu ? TileG::BN / 2 : TileG::BN;
-  const int64_t rows = send_rows < h_rows ? send_rows : h_rows;
-  const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((a.n_out + outc - 1) / outc);
-  return glu ? run_grouped<kSwiglu, false>(a, max_tiles, stream)
-             : run_grouped<kLinear, false>(a, max_tiles, stream);
-}
-
-extern "C" int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* recv_counts,
-                               const int32_t* send_counts, int world_size_src, int ep_rank,
-                               int num_experts, int local_experts, const void* w2, int64_t I,
-                               int64_t H, void* combine_buf, int64_t combine_rows,
-                               int32_t* dev_err, hipStream_t stream) {
-  if (!h || !send_counts || !recv_counts || !w2 || !combine_buf) return MC2_ERR_NULL;
-  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
-  if (st) return st;
-  if (I < 1 || H < 8 || h_rows < 0 || combine_rows < 0) return MC2_ERR_SHAPE;
-  if (I % 8 || H % 8) return MC2_ERR_ALIGN;
-  if (!aligned16(h) || !aligned16(w2) || !aligned16(combine_buf)) return MC2_ERR_ALIGN;
-  if (!offsets_fit(I * 2, H * 2)) return MC2_ERR_UNSUPPORTED;
-  GroupedArgs a{};
-  a.A = static_cast<const char*>(h);
-  a.lda = I * 2;
-  a.B = static_cast<const char*>(w2);
-  a.ldb = H * 2;
-  a.b_group = I * H * 2;
-  a.out = static_cast<char*>(combine_buf);
-  a.n_b = H;
-  a.n_out = H;
-  a.inter = 0;
-  a.ldo = H * 2;
-  a.K = I;
-  a.send_counts = send_counts;
-  a.recv_counts = recv_counts;
-  a.ep_rank = ep_rank;
-  a.num_experts = num_experts;
-  a.local_experts = local_experts;
-  a.combine = 1;
-  a.a_cap = h_rows;
-  a.o_cap = combine_rows;
-  a.dev_err = dev_err;
-  a.ktiles = static_cast<int>((I + 63) / 64);
-  const int64_t rows = h_rows < combine_rows ? h_rows : combine_rows;
-  const int64_t max_tiles =
-      (rows / TileG::BM + local_experts) * ((H + TileG::BN - 1) / TileG::BN);
-  return run_grouped<kLinear, false>(a, max_tiles, stream);
-}
-
-// ---------------------------------------------------------------- EP backward
-
-namespace mc2 {
-
-// Elements per row of the transposed workspace: every group padded to 64,
-// and the row pitch a multiple of 128 bytes.
-static int64_t backward_kt(int64_t rows, int local_experts) {
-  return (rows + kGroupAlign * static_cast<int64_t>(local_experts) + kGroupAlign - 1) &
-         ~int64_t{kGroupAlign - 1};
-}
-
-// Workspace of a weight gradient dW = P^T Q over `rows` rows of P, dW (E_l,
-// M, N): the transposed rows (M x kt bf16), then the tile counters, then the
-// partial-tile slots of split groups. A split group of c > L rows has
-// ceil(c / L) < 2c / L slices, so 2 * rows / L slots always suffice.
-struct WgradLayout {
-  int64_t kt, tiles_m, tiles_n, max_slots;
-  size_t off_ctr, off_part, total;
-};
-
-static WgradLayout wgrad_layout(int64_t rows, int local_experts, int64_t M, int64_t N) {
-  WgradLayout w{};
-  w.kt = backward_kt(rows, local_experts);
-  w.tiles_m = (M + TileL::BM - 1) / TileL::BM;
-  w.tiles_n = (N + TileL::BN - 1) / TileL::BN;
-  w.max_slots = 2 * rows / kSliceRows;
-  const size_t per_group = static_cast<size_t>(w.tiles_m * w.tiles_n);
-  w.off_ctr = (static_cast<size_t>(M) * static_cast<size_t>(w.kt) * 2 + 255) & ~size_t{255};
-  w.off_part = (w.off_ctr + per_group * local_experts * 4 + 255) & ~size_t{255};
-  w.total = w.off_part + static_cast<size_t>(w.max_slots) * per_group * TileL::BM * TileL::BN * 4;
-  return w;
-}
-
-static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, const char* Q,
-                     int64_t ldq, int q_at_send, int64_t q_cap, int64_t M, int64_t N,
-                     const int32_t* send_counts, const int32_t* recv_counts, int ep_rank,
-                     int local_experts, float* dw, void* workspace, int32_t* dev_err,
-                     hipStream_t stream) {
-  const WgradLayout L = wgrad_layout(p_cap, local_experts, M, N);
-  char* ws = static_cast<char*>(workspace);
-  const int64_t per_group = L.tiles_m * L.tiles_n;
-  TransposeArgs t{};
-  t.P = P;
-  t.ldp = ldp;
-  t.at_send = p_at_send;
-  t.cols = M;
-  t.p_cap = p_cap;
-  t.PT = ws;
-  t.kt = L.kt;
-  t.send_counts = send_counts;
-  t.recv_counts = recv_counts;
-  t.ep_rank = ep_rank;
-  t.local_experts = local_experts;
-  t.dev_err = dev_err;
-  t.zero = reinterpret_cast<uint32_t*>(ws + L.off_ctr);
-  t.n_zero = per_group * local_experts;
-  // 64-row blocks; the column blocks are split over a few workgroups only
-  // when there are too few row blocks to fill the chip
-  const int64_t rb = (p_cap + 63) / 64;
-  int64_t cb = (M + 63) / 64;
-  const int64_t want = (4 * static_cast<int64_t>(num_cus()) + rb - 1) / (rb > 0 ? rb : 1);
-  cb = cb < want ? cb : want;
-  cb = cb < 1 ? 1 : cb;
-  if (rb > 0x7fffffff) return MC2_ERR_SHAPE;
-  hipLaunchKernelGGL(group_transpose_kernel,
-                     dim3(static_cast<unsigned>(rb > 0 ? rb : 1), static_cast<unsigned>(cb)),
-                     dim3(512), 0, stream, t);
-  if (hipGetLastError() != hipSuccess) return MC2_ERR_HIP;
-  WgradArgs w{};
-  w.PT = ws;
-  w.ldpt = L.kt * 2;
-  w.Q = Q;
-  w.ldq = ldq;
-  w.at_send = q_at_send;
-  w.q_cap = q_cap;
-  w.out = dw;
-  w.M = M;
-  w.N = N;
-  w.tiles_m = static_cast<int>(L.tiles_m);
-  w.tiles_n = static_cast<int>(L.tiles_n);
-  w.round = static_cast<int>(num_cus() / 8 * 8);
-  w.counters = t.zero;
-  w.partials = reinterpret_cast<float*>(ws + L.off_part);
-  w.max_slots = L.max_slots;
-  w.send_counts = send_counts;
-  w.recv_counts = recv_counts;
-  w.ep_rank = ep_rank;
-  w.local_experts = local_experts;
-  w.dev_err = dev_err;
-  // at most rows / L + E_l slices in all
-  const int64_t units = (p_cap / kSliceRows + local_experts) * per_group;
-  if (units > 0x3fffffff) return MC2_ERR_SHAPE;
-  hipLaunchKernelGGL((wgrad_kernel<TileL>), dim3(static_cast<unsigned>(units)), dim3(kThreads), 0,
-                     stream, w);
-  return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
-}
-
-}  // namespace mc2
-
-extern "C" size_t mc2_gmm_backward_workspace_size(int64_t rows, int local_experts, int64_t M,
-                                                  int64_t N) {
-  if (rows < 0 || M < 1 || N < 1 || local_experts < 1 || local_experts > kMaxLocalExperts) return 0;
-  return wgrad_layout(rows, local_experts, M, N).total;
-}
-
-extern "C" int mc2_gmm_combine_backward(const void* dy_buf, int64_t dy_rows,
-                                        const int32_t* recv_counts, const int32_t* send_counts,
-                                        int world_size_src, int ep_rank, int num_experts,
-                                        int local_experts, const void* w2, int64_t I, int64_t H,
-                                        const void* h, int64_t h_rows, const void* g_saved, int act,
-                                        void* dgrad_out, float* dw2_out, void* workspace,
-                                        size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
-  if (!dy_buf || !send_counts || !recv_counts || !w2 || !h || !dgrad_out || !dw2_out)
-    return MC2_ERR_NULL;
-  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
-  if (st) return st;
-  if (I < 8 || H < 8 || dy_rows < 0 || h_rows < 0) return MC2_ERR_SHAPE;
-  if (act != MC2_ACT_NONE && act != MC2_ACT_SWIGLU) return MC2_ERR_SHAPE;
-  const bool glu = act == MC2_ACT_SWIGLU;
-  if (glu && !g_saved) return MC2_ERR_NULL;
-  if (I % 8 || H % 8) return MC2_ERR_ALIGN;
-  if (!aligned16(dy_buf) || !aligned16(w2) || !aligned16(h) || !aligned16(dgrad_out) ||
-      !aligned16(dw2_out) || (glu && !aligned16(g_saved)))
-    return MC2_ERR_ALIGN;
-  if (!workspace) return MC2_ERR_NULL;
-  if (!aligned16(workspace)) return MC2_ERR_ALIGN;
-  if (ws_bytes < mc2_gmm_backward_workspace_size(h_rows, local_experts, I, H)) return MC2_ERR_WORKSPACE;
-  if (!offsets_fit(H * 2, H * 2) || !offsets_fit(backward_kt(h_rows, local_experts) * 2, H * 2))
-    return MC2_ERR_UNSUPPORTED;
-  // dgrad: dA = dY_g @ w2[g]^T, the weight read as (I, H) rows; SwiGLU backward fused
-  GroupedArgs a{};
-  a.A = static_cast<const char*>(dy_buf);
-  a.lda = H * 2;
-  a.B = static_cast<const char*>(w2);
-  a.ldb = H * 2;
-  a.b_group = I * H * 2;
-  a.out = static_cast<char*>(dgrad_out);
-  a.n_b = I;
-  a.n_out = I;
-  a.inter = I;
-  a.ldo = (glu ? 2 * I : I) * 2;
-  a.K = H;
-  a.send_counts = send_counts;
-  a.recv_counts = recv_counts;
-  a.ep_rank = ep_rank;
-  a.num_experts = num_experts;
-  a.local_experts = local_experts;
-  a.combine = 0;
-  a.a_cap = dy_rows;
-  a.o_cap = h_rows;
-  a.dev_err = dev_err;
-  a.ktiles = static_cast<int>((H + 63) / 64);
-  a.gsave = static_cast<const char*>(g_saved);
-  a.ldg = 2 * I * 2;
-  const int64_t rows = dy_rows < h_rows ? dy_rows : h_rows;
-  const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((I + TileG::BN - 1) / TileG::BN);
-  st = glu ? run_grouped<kSwigluBwd, true>(a, max_tiles, stream)
-           : run_grouped<kLinear, true>(a, max_tiles, stream);
-  if (st) return st;
-  // wgrad: dW2[g] = h_g^T @ dY_g
-  return run_wgrad(static_cast<const char*>(h), I * 2, 0, h_rows, static_cast<const char*>(dy_buf),
-                   H * 2, 1, dy_rows, I, H, send_counts, recv_counts, ep_rank, local_experts,
-                   dw2_out, workspace, dev_err, stream);
-}
-
-extern "C" int mc2_gmm_dispatch_backward(const void* dg, int64_t dg_rows, const int32_t* recv_counts,
-                                         const int32_t* send_counts, int world_size_src,
-                                         int ep_rank, int num_experts, int local_experts,
-                                         const void* w1, int64_t H, int64_t I2,
-                                         const void* send_buf, int64_t send_rows, void* dx_buf,
-                                         int64_t dx_rows, float* dw1_out, void* workspace,
-                                         size_t ws_bytes, int32_t* dev_err, hipStream_t stream) {
-  if (!dg || !send_counts || !recv_counts || !w1 || !send_buf || !dx_buf || !dw1_out)
-    return MC2_ERR_NULL;
-  int st = check_ep(world_size_src, ep_rank, num_experts, local_experts);
-  if (st) return st;
-  if (H < 8 || I2 < 8 || dg_rows < 0 || send_rows < 0 || dx_rows < 0) return MC2_ERR_SHAPE;
-  if (H % 8 || I2 % 8) return MC2_ERR_ALIGN;
-  if (!aligned16(dg) || !aligned16(w1) || !aligned16(send_buf) || !aligned16(dx_buf) ||
-      !aligned16(dw1_out))
-    return MC2_ERR_ALIGN;
-  if (!workspace) return MC2_ERR_NULL;
-  if (!aligned16(workspace)) return MC2_ERR_ALIGN;
-  if (ws_bytes < mc2_gmm_backward_workspace_size(send_rows, local_experts, H, I2))
-    return MC2_ERR_WORKSPACE;
-  if (!offsets_fit(I2 * 2, I2 * 2) || !offsets_fit(backward_kt(send_rows, local_experts) * 2, I2 * 2))
-    return MC2_ERR_UNSUPPORTED;
-  // dgrad: dX_g = dG_g @ w1[g]^T, the weight read as (H, I2) rows, written at the send rows
-  GroupedArgs a{};
-  a.A = static_cast<const char*>(dg);
-  a.lda = I2 * 2;
-  a.B = static_cast<const char*>(w1);
-  a.ldb = I2 * 2;
-  a.b_group = H * I2 * 2;
-  a.out = static_cast<char*>(dx_buf);
-  a.n_b = H;
-  a.n_out = H;
-  a.inter = 0;
-  a.ldo = H * 2;
-  a.K = I2;
-  a.send_counts = send_counts;
-  a.recv_counts = recv_counts;
-  a.ep_rank = ep_rank;
-  a.num_experts = num_experts;
-  a.local_experts = local_experts;
-  a.combine = 1;
-  a.a_cap = dg_rows;
-  a.o_cap = dx_rows;
-  a.dev_err = dev_err;
-  a.ktiles = static_cast<int>((I2 + 63) / 64);
-  const int64_t rows = dg_rows < dx_rows ? dg_rows : dx_rows;
-  const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((H + TileG::BN - 1) / TileG::BN);
-  st = run_grouped<kLinear, true>(a, max_tiles, stream);
-  if (st) return st;
-  // wgrad: dW1[g] = R_g^T @ dG_g over this rank's send rows R
-  return run_wgrad(static_cast<const char*>(send_buf), H * 2, 1, send_rows,
-                   static_cast<const char*>(dg), I2 * 2, 0, dg_rows, H, I2, send_counts,
-                   recv_counts, ep_rank, local_experts, dw1_out, workspace, dev_err, stream);
 }
