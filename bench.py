@@ -38,6 +38,7 @@ PEAK_HBM = 8000.0    # GB/s, HBM3E (published)
 # the sources of the headline kernel (the grouped and MoE kernels live elsewhere)
 KERNEL_SOURCES = ["gemm_collective_core_amd/csrc/gemm_core.hpp",
                   "gemm_collective_core_amd/csrc/mc2_tiles.hpp",
+                  "gemm_collective_core_amd/csrc/mc2_chunked.hpp",
                   "gemm_collective_core_amd/csrc/mc2_gemm.hip",
                   "gemm_collective_core_amd/csrc/mc2_common.hpp",
                   "gemm_collective_core_amd/csrc/mc2_host.hpp"]

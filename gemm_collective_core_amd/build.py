@@ -14,7 +14,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmc2.so")
-SOURCES = ["mc2_gemm.hip", "mc2_grouped.hip", "mc2_moe.hip"]
+SOURCES = ["mc2_gemm.hip", "mc2_allreduce.hip", "mc2_grouped.hip", "mc2_moe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
