@@ -548,6 +548,28 @@ def _bf(vals):
     return (np.asarray(vals, np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
+def test_ar_sum_rank_rounded_is_the_correctly_rounded_exact_sum():
+    """W = 32 bf16 partials (8-bit significands) within 10 binades: their exact
+    sum needs at most 8 + 10 + 5 bits, so math.fsum (computed without the
+    oracle) gives it exactly, it is exact in float32 too, and torch's
+    float32 -> bf16 cast is then its one correct rounding. The rank-rounded
+    combine must equal it. Catches a dropped partial, a wrong rounding and a
+    per-hop rounding."""
+    rng = np.random.default_rng(21)
+    W, n = 32, 500
+    vals = (rng.standard_normal((W, n)) * np.exp2(rng.integers(-5, 5, (W, n)))).astype(np.float32)
+    parts = bf16_bits(vals)
+    got = gemm.ar_sum(parts, dtype="bf16", rounding=gemm.AR_RANK_ROUNDED)
+    dec = torch.from_numpy(parts.view(np.int16)).view(torch.bfloat16).double().numpy()
+    exact = np.array([math.fsum(dec[:, j]) for j in range(n)])
+    assert np.array_equal(exact.astype(np.float32).astype(np.float64), exact)
+    want = torch.from_numpy(exact.astype(np.float32)).to(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(got, want)
+    # and the hop-rounded combine is not the same function
+    hop = gemm.ar_sum(parts, dtype="bf16", rounding=gemm.AR_HOP_ROUNDED)
+    assert not np.array_equal(hop, want)
+
+
 def test_mm_ar_rounding_modes_hand_worked_bf16():
     """bf16 spacing at 1 is 2**-7. Rank 0's partial 1 + 2**-8 sits exactly half
     way between 1 and 1 + 2**-7 and rounds (ties to even) to 1; rank 1's partial
