@@ -557,7 +557,10 @@ def test_ar_sum_rank_rounded_is_the_correctly_rounded_exact_sum():
     per-hop rounding."""
     rng = np.random.default_rng(21)
     W, n = 32, 500
-    vals = (rng.standard_normal((W, n)) * np.exp2(rng.integers(-5, 5, (W, n)))).astype(np.float32)
+    # sign * m * 2^(e - 7) with m in [128, 256): exponents e in [-5, 5)
+    m = rng.integers(128, 256, (W, n)).astype(np.float64)
+    e = rng.integers(-5, 5, (W, n))
+    vals = (rng.choice([-1.0, 1.0], (W, n)) * m * np.exp2(e - 7)).astype(np.float32)
     parts = bf16_bits(vals)
     got = gemm.ar_sum(parts, dtype="bf16", rounding=gemm.AR_RANK_ROUNDED)
     dec = torch.from_numpy(parts.view(np.int16)).view(torch.bfloat16).double().numpy()
