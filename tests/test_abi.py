@@ -179,3 +179,33 @@ def test_gmm_backward_validates(lib):
     assert Db(*dbase, FAKE + 8, 1 << 24, None, None) == ERR_ALIGN
     assert Db(*dbase[:15], None, FAKE, 1 << 24, None, None) == ERR_NULL
     assert Db(*dbase[:5], 4, *dbase[6:], FAKE, 1 << 24, None, None) == ERR_SHAPE     # ep_rank < E / E_l
+
+
+def test_header_is_plain_c_and_links_from_c(tmp_path):
+    """The ABI is a C ABI: the header compiles as C99 and a C program links
+    against the built library and calls it (entry points that need no GPU)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no C compiler")
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "mc2.h"\n'
+        'int main(void) {\n'
+        '  printf("%s|%s|%d\\n", mc2_version(), mc2_status_string(MC2_ERR_SHAPE),\n'
+        '         mc2_mm_rs_local(0, 0, 1, 1, 1, 1, 0, 1, 0, MC2_BF16, 0, 0, 0, MC2_BF16, 0, 0, 0,\n'
+        '                         0, 0, 0));\n'
+        '  return 0;\n}\n')
+    libdir = os.path.dirname(_lib.LIB_PATH)
+    exe = tmp_path / "use"
+    cmd = [gcc, "-std=c99", "-D__HIP_PLATFORM_AMD__", "-I", os.path.dirname(HEADER),
+           "-I", "/opt/rocm/include", str(src), "-o", str(exe), "-L", libdir, "-lmc2",
+           "-Wl,-rpath," + libdir]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    version, status, code = out.stdout.strip().split("|")
+    assert version.startswith("mc2-gfx950") and status.startswith("MC2_")
+    assert int(code) == 1  # MC2_ERR_NULL: x1 is NULL
