@@ -337,16 +337,19 @@ struct TransposeArgs {
 };
 
 // PT[c][pstart[g] + i] = P[base + gstart[g] + i][c] for every local group g
-// and row i < count g; the up-to-7 columns after each group are zeroed, so
-// that a 16-byte K piece read past the group's last row holds zeros. One
-// workgroup takes 64 rows and walks over the columns in 64-column blocks,
-// each through LDS: 16-byte loads along the rows, then each wave writes 64
-// consecutive columns of one PT row.
+// and row i < count g, and zeros in the columns after each group up to the next
+// multiple of 64, so that a 16-byte K piece read past the group's last row
+// holds zeros. Workgroup x takes a 64-row block of one group (blocks start at
+// the group's first row, so the block's destination columns start on a
+// 128-byte line) and walks over the columns in 64-column tiles, each through
+// LDS: 16-byte loads along the rows, then every thread gathers 8 rows of one
+// column and writes them with one 16-byte store. The grid may have more
+// blocks than the groups need (the host knows only a bound); the rest exit.
 __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
   __shared__ GroupTable t;
-  constexpr int pitch = 132;  // bytes per LDS row: 64 bf16 + 4, so a column read is conflict-free
+  __shared__ int64_t s_bstart[kMaxLocalExperts + 1];
+  constexpr int pitch = 132;  // bytes per LDS row: 64 bf16 + 4, so column reads are conflict-free
   __shared__ __attribute__((aligned(16))) char tile_raw[64 * pitch];
-  __shared__ int64_t s_dcol[64];
   lds_t* tile = (lds_t*)tile_raw;
   if (blockIdx.x == 0 && blockIdx.y == 0)
     for (int64_t i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero[i] = 0u;
@@ -358,50 +361,50 @@ __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
     if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
     return;
   }
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x) * 64;
-  if (r0 >= n) return;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int64_t r = r0 + tid;
-    int g = 0;
-    while (g + 1 < El && t.gstart[g + 1] <= r) ++g;
-    s_dcol[tid] = r < n ? t.pstart[g] + (r - t.gstart[g]) : -1;
+  if (threadIdx.x == 0) {
+    int64_t b = 0;
+    for (int e = 0; e < El; ++e) {
+      s_bstart[e] = b;
+      b += (t.cnt[e] + 63) / 64;
+    }
+    s_bstart[El] = b;
   }
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int64_t dcol = s_dcol[lane];
+  const int64_t blk = blockIdx.x;
+  if (blk >= s_bstart[El]) return;
+  int g = 0;
+  while (g + 1 < El && s_bstart[g + 1] <= blk) ++g;
+  const int64_t j64 = (blk - s_bstart[g]) * 64;       // first row of the block within group g
+  const int64_t nr = t.cnt[g] - j64 < 64 ? t.cnt[g] - j64 : 64;
+  const int64_t src0 = base + t.gstart[g] + j64;      // first source row
+  const int64_t dst0 = t.pstart[g] + j64;             // first destination column (64-aligned)
+  const int tid = threadIdx.x;
+  const int lr = tid >> 3, ch = tid & 7;              // load: row, 16-byte chunk
+  const int oc = tid >> 3, r8 = (tid & 7) * 8;        // store: column, first of 8 rows
   for (int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64; c0 < p.cols; c0 += 64 * gridDim.y) {
     {
-      const int r = tid >> 3, ch = tid & 7;
-      const int64_t gr = r0 + r, gc = c0 + ch * 8;
+      const int64_t gc = c0 + ch * 8;
       u32x4_t v = zero_v4();
-      if (gr < n && gc < p.cols)
+      if (lr < nr && gc < p.cols)
         v = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(p.P + (base + gr) * p.ldp + gc * 2));
+            reinterpret_cast<const u32x4_t*>(p.P + (src0 + lr) * p.ldp + gc * 2));
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<MC2_LDS uint32_t*>(tile + r * pitch + ch * 16 + j * 4) = v[j];
+        *reinterpret_cast<MC2_LDS uint32_t*>(tile + lr * pitch + ch * 16 + j * 4) = v[j];
     }
     __syncthreads();
-    for (int k = 0; k < 8; ++k) {
-      const int c = wave * 8 + k;
-      if (c0 + c >= p.cols) break;
-      if (dcol >= 0)
-        *reinterpret_cast<uint16_t*>(p.PT + (c0 + c) * p.kt * 2 + dcol * 2) =
-            *reinterpret_cast<const MC2_LDS uint16_t*>(tile + lane * pitch + c * 2);
-    }
-    // zero the padding after every group whose last row lies in this block
-    for (int g = 0; g < El; ++g) {
-      const int64_t last = t.gstart[g + 1] - 1;
-      if (t.gstart[g + 1] == t.gstart[g] || last < r0 || last >= r0 + 64) continue;
-      const int64_t pad0 = t.pstart[g] + (t.gstart[g + 1] - t.gstart[g]);
-      const int64_t pad1 = (pad0 + 7) & ~int64_t{7};
-      const int npad = static_cast<int>(pad1 - pad0);
-      for (int q = tid; q < 64 * 8; q += blockDim.x) {
-        const int c = q >> 3, j = q & 7;
-        if (j < npad && c0 + c < p.cols)
-          *reinterpret_cast<uint16_t*>(p.PT + (c0 + c) * p.kt * 2 + (pad0 + j) * 2) = 0;
+    if (c0 + oc < p.cols) {
+      u32x4_t w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t lo = *reinterpret_cast<const MC2_LDS uint16_t*>(tile + (r8 + 2 * j) * pitch + oc * 2);
+        const uint32_t hi =
+            *reinterpret_cast<const MC2_LDS uint16_t*>(tile + (r8 + 2 * j + 1) * pitch + oc * 2);
+        w[j] = lo | (hi << 16);
       }
+      // rows past the group's end were loaded as zeros: they pad the group
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<u32x4_t*>(p.PT + ((c0 + oc) * p.kt + dst0 + r8) * 2));
     }
     __syncthreads();
   }
@@ -726,9 +729,10 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   t.dev_err = dev_err;
   t.zero = reinterpret_cast<uint32_t*>(ws + L.off_ctr);
   t.n_zero = per_group * local_experts;
-  // 64-row blocks; the column blocks are split over a few workgroups only
-  // when there are too few row blocks to fill the chip
-  const int64_t rb = (p_cap + 63) / 64;
+  // 64-row blocks, each inside one group (at most rows / 64 + E_l of them);
+  // the column tiles are split over a few workgroups only when there are too
+  // few row blocks to fill the chip
+  const int64_t rb = p_cap / 64 + local_experts;
   int64_t cb = (M + 63) / 64;
   const int64_t want = (4 * static_cast<int64_t>(num_cus()) + rb - 1) / (rb > 0 ? rb : 1);
   cb = cb < want ? cb : want;
