@@ -284,6 +284,16 @@ struct GroupTable {
   int bad;
 };
 
+// Values read from shared memory are per-lane as far as the compiler knows;
+// the ones that feed buffer descriptors and loop bounds are made wave-uniform
+// (scalar registers), or every load would run in a per-lane loop.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __device__ __forceinline__ void load_group_table(GroupTable& t, const int32_t* send_counts,
                                                  const int32_t* recv_counts, int ep_rank, int El) {
   const int tid = threadIdx.x;
@@ -480,24 +490,27 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
     s_slot[El] = slot;
   }
   __syncthreads();
-  const int64_t base = p.at_send ? t.base : 0;
+  const int64_t base = p.at_send ? uni(t.base) : 0;
   if (t.bad || base + t.gstart[El] > p.q_cap || s_slot[El] > p.max_slots) {
     if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
     return;
   }
   const int64_t u = xcd_tile(blockIdx.x, p.round, gridDim.x);
-  if (u >= s_ustart[El]) return;
+  if (u >= uni(s_ustart[El])) return;
   int q = 0;
   while (q + 1 < El && s_ustart[q + 1] <= u) ++q;
-  const int g = s_order[q];
-  const int64_t lu = u - s_ustart[q];
-  const int s = static_cast<int>(lu / per_group);
-  const int lt = static_cast<int>(lu - static_cast<int64_t>(s) * per_group);
-  const int tm = lt % p.tiles_m, tn = lt / p.tiles_m;
+  q = uni(q);
+  const int g = uni(s_order[q]);
+  const int64_t lu = u - uni(s_ustart[q]);
+  // 64-bit division runs on the vector ALU: its results are made uniform again
+  const int s = uni(static_cast<int>(lu / per_group));
+  const int lt = uni(static_cast<int>(lu - static_cast<int64_t>(s) * per_group));
+  const int tm = uni(lt % p.tiles_m), tn = uni(lt / p.tiles_m);
   const int64_t row0 = static_cast<int64_t>(tm) * TS::BM;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
-  const int64_t cnt = t.cnt[g];
-  const int64_t nslices = (s_ustart[q + 1] - s_ustart[q]) / per_group;
+  const int64_t cnt = uni(static_cast<int64_t>(t.cnt[g]));
+  const int64_t nslices = (uni(s_ustart[q + 1]) - uni(s_ustart[q])) / per_group;
+  const int64_t gstart = uni(t.gstart[g]), pstart = uni(t.pstart[g]);
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
   if (cnt == 0) {
@@ -512,9 +525,9 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   const int ktiles = static_cast<int>((klen + 63) / 64);
   KSpan ks{klen, 0, 0, ktiles, ktiles};
   f32x4_t acc[TS::FM][TS::FN];
-  BDesc bd{p.Q + (base + t.gstart[g] + k0) * p.ldq, p.ldq, p.N};
+  BDesc bd{p.Q + (base + gstart + k0) * p.ldq, p.ldq, p.N};
   PlainCols cm{col0, p.N - 8};
-  mainloop<Elem::BF16, false, TS>(smem, p.PT + (t.pstart[g] + k0) * 2, p.ldpt, row0, p.M - 1, bd,
+  mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
                                   col0, cm, ks, acc);
   if (nslices == 1) {
     char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
@@ -527,7 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   }
   // split group: this slice's partial tile (dense BM x BN) into its slot
   constexpr int64_t kTileElems = static_cast<int64_t>(TS::BM) * TS::BN;
-  float* part0 = p.partials + (s_slot[g] * per_group + lt) * kTileElems;
+  float* part0 = p.partials + (uni(s_slot[g]) * per_group + lt) * kTileElems;
   const int64_t slice_stride = per_group * kTileElems;
   char* mine = reinterpret_cast<char*>(part0 + s * slice_stride);
   epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
