@@ -38,6 +38,16 @@ __device__ __forceinline__ void stage_swiglu(lds_t* smem, int pitch,
 
 // ---------------------------------------------------------------- grouped GEMM
 
+// Values read from shared memory are per-lane as far as the compiler knows;
+// the ones that feed buffer descriptors and loop bounds are made wave-uniform
+// (scalar registers), or every load would run in a per-lane loop.
+__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int64_t uni(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 constexpr int kMaxLocalExperts = 256;
 
 struct GroupedArgs {
@@ -215,9 +225,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
       return;
     }
   }
-  const int64_t a_base = p.combine ? 0 : s_base;
-  const int64_t o_base = p.combine ? s_base : 0;
-  const int64_t total = s_tstart[El];
+  const int64_t a_base = p.combine ? 0 : uni(s_base);
+  const int64_t o_base = p.combine ? uni(s_base) : 0;
+  const int64_t total = uni(s_tstart[El]);
 
   KSpan ks{p.K, 0, 0, p.ktiles, p.ktiles};
   // With one workgroup per CU (a multiple of 8), XCD x takes tiles 32x ..
@@ -227,13 +237,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
   for (int64_t t = tfirst; t < total; t += gridDim.x) {
     int g = 0;
     while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
-    const int64_t cnt = s_gstart[g + 1] - s_gstart[g];
+    g = uni(g);
+    const int64_t gs = uni(s_gstart[g]);
+    const int64_t cnt = uni(s_gstart[g + 1]) - gs;
     const int64_t tiles_m = (cnt + TS::BM - 1) / TS::BM;
-    const int64_t lt = t - s_tstart[g];
-    const int64_t tm = lt % tiles_m, tn = lt / tiles_m;
-    const int64_t arow0 = a_base + s_gstart[g] + tm * TS::BM;
-    const int64_t arow_end = a_base + s_gstart[g] + cnt;
-    const int64_t orow0 = o_base + s_gstart[g] + tm * TS::BM;
+    const int64_t lt = t - uni(s_tstart[g]);
+    // 64-bit division runs on the vector ALU: its results are made uniform again
+    const int64_t tm = uni(lt % tiles_m), tn = uni(lt / tiles_m);
+    const int64_t arow0 = a_base + gs + tm * TS::BM;
+    const int64_t arow_end = a_base + gs + cnt;
+    const int64_t orow0 = o_base + gs + tm * TS::BM;
     const int64_t ocol0 = tn * OUTC;
 
     f32x4_t acc[TS::FM][TS::FN];
@@ -283,16 +296,6 @@ struct GroupTable {
   int64_t base;
   int bad;
 };
-
-// Values read from shared memory are per-lane as far as the compiler knows;
-// the ones that feed buffer descriptors and loop bounds are made wave-uniform
-// (scalar registers), or every load would run in a per-lane loop.
-__device__ __forceinline__ int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
-__device__ __forceinline__ int64_t uni(int64_t v) {
-  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
-  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
-  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
-}
 
 __device__ __forceinline__ void load_group_table(GroupTable& t, const int32_t* send_counts,
                                                  const int32_t* recv_counts, int ep_rank, int El) {
