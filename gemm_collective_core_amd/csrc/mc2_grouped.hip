@@ -517,8 +517,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
   if (cnt == 0) {
-    for (int q = threadIdx.x; q < TS::BM * TS::BN; q += kThreads) {
-      const int r = q / TS::BN, c = q - r * TS::BN;
+    for (int i = threadIdx.x; i < TS::BM * TS::BN; i += kThreads) {
+      const int r = i / TS::BN, c = i - r * TS::BN;
       if (r < nrows && c < ncols) dst[(row0 + r) * p.N + col0 + c] = 0.0f;
     }
     return;
@@ -561,8 +561,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int q = threadIdx.x; q < TS::BM * TS::BN / 4; q += kThreads) {
-    const int r = q / (TS::BN / 4), c = (q - r * (TS::BN / 4)) * 4;
+  for (int i = threadIdx.x; i < TS::BM * TS::BN / 4; i += kThreads) {
+    const int r = i / (TS::BN / 4), c = (i - r * (TS::BN / 4)) * 4;
     if (r >= nrows || c >= ncols) continue;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int64_t j = 0; j < nslices; ++j) {
