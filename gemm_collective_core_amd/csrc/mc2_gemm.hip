@@ -37,6 +37,7 @@ struct ChunkedArgs {
   uint32_t spin_limit;
   int32_t* dev_err;
   int own_chunk;             // the chunk that needs no input flag
+  int store_wt;              // 16-bit outputs written through to memory (flags raised)
 };
 
 // Waits (one thread polls) until input segment g is marked ready, then acquires
@@ -119,7 +120,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
                               [&](int r, int cc, float v) { put_out<O>(smem + r * pitch + cc * OS, v); });
     __syncthreads();
     store_staged(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo, row_end - row0,
-                 col0 * OS, p.n * OS);
+                 col0 * OS, p.n * OS, p.store_wt != 0);
   } else {
     // 32-bit test outputs: stored straight from the accumulator layout.
     char* base = p.out + row0 * p.ldo + col0 * OS;
@@ -275,6 +276,9 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   a.flags = flags;
   a.counters = counters;
   a.epoch = epoch;
+  // a tile's stores address at most 256 rows from its first: the buffer offsets
+  // of the write-through path stay below 2^31
+  a.store_wt = flags != nullptr && a.ldo * 256 < 0x7fff0000LL;
   a.in_flags = inw.flags;
   a.in_epoch = inw.epoch;
   a.spin_limit = inw.spin_limit;
