@@ -33,9 +33,9 @@ PEAK_BF16 = 2500.0   # TFLOP/s, dense bf16/fp16 MFMA (published)
 PEAK_I8 = 5000.0     # TOP/s, dense int8 MFMA (published)
 PEAK_HBM = 8000.0    # GB/s, HBM3E (published)
 
-# Sources of the headline kernel: the HBM traffic recorded under profiles/ is
-# reported only while these files are unchanged since the counters were taken.
-# the sources of the headline kernel (the grouped and MoE kernels live elsewhere)
+# Sources of the headline kernel (the grouped and MoE kernels live elsewhere):
+# the HBM traffic recorded under profiles/ is reported only while their code,
+# comments and blank space aside, is unchanged since the counters were taken.
 KERNEL_SOURCES = ["gemm_collective_core_amd/csrc/gemm_core.hpp",
                   "gemm_collective_core_amd/csrc/mc2_tiles.hpp",
                   "gemm_collective_core_amd/csrc/mc2_chunked.hpp",
@@ -46,11 +46,17 @@ TRAFFIC_FILE = "profiles/traffic_ag_mm_bf16_8192x3072x3072.json"
 
 
 def kernel_source_hash():
+    """sha256 of the headline kernel's sources with comments removed and
+    blank space collapsed, so that a change to comments alone keeps it."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

@@ -2,8 +2,9 @@
 //
 // Workgroup: 8 waves = 512 threads, two waves per SIMD, computing a BM x BN
 // output tile (256 x 256 or 128 x 256); wave (wm, wn) owns a WTM x WTN
-// sub-tile. Two waves per SIMD roughly double the loads a CU keeps in flight,
-// and the per-CU load rate is what bounds a GEMM tile on this chip.
+// sub-tile. Two waves per SIMD let one wave's MFMAs run while the other waits
+// on its operand reads or on a load instruction the memory pipeline has not
+// yet taken.
 //
 // K advances in stages of 128 bytes per row (64 bf16/fp16 or 128 int8
 // values, two MFMA k-steps) held in a two-buffer LDS ring. Loads go straight
