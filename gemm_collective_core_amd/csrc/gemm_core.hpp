@@ -71,7 +71,7 @@ struct Tile {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "tile not divisible");
-  static_assert(BN == 256 && BM % 64 == 0, "row-major B loads cover whole 256-column rows");
+  static_assert((BN == 256 || BN == 192) && BM % 64 == 0, "tile shapes of the load mapping");
   static constexpr int kABytes = BM * kKBytes;
   static constexpr int kBBytes = BN * kKBytes;  // same size in both B layouts
   static constexpr int kStageBytes = kABytes + kBBytes;
@@ -124,6 +124,32 @@ __device__ __forceinline__ int row_off(int r, int c) {
 // k-major swizzles: 16-bit rows (512 bytes) move 32-byte pairs, 8-bit rows
 // (256 bytes) move 16-byte chunks.
 __device__ __forceinline__ int kmaj_swz16(int kr) { return (kr & 3) | (((kr >> 3) & 1) << 2); }
+
+// Position of 32-byte pair p (16 columns) in 16-bit k row kr of a tile BN
+// columns wide, and its inverse. 512-byte rows: XOR with kmaj_swz16. 384-byte
+// rows (12 pairs): rotation by ((kr >> 1) & 1) | ((kr >> 3) & 1) << 1. A row
+// of 384 bytes moves the bank by 4 32-byte groups per row (12 mod 8), so the
+// 8 rows one half-wave of a transposing read touches (kr & 3 and bit 3 of kr
+// taking all 8 values) land on 4 * (kr & 1) + rotation + p mod 8: all 8
+// groups, once each.
+template <int BN>
+__device__ __forceinline__ int kmaj_pos16(int p, int kr) {
+  if constexpr (BN == 256) {
+    return p ^ kmaj_swz16(kr);
+  } else {
+    const int q = p + (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
+    return q < 12 ? q : q - 12;
+  }
+}
+template <int BN>
+__device__ __forceinline__ int kmaj_unpos16(int pp, int kr) {
+  if constexpr (BN == 256) {
+    return pp ^ kmaj_swz16(kr);
+  } else {
+    const int q = pp - (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
+    return q >= 0 ? q : q + 12;
+  }
+}
 __device__ __forceinline__ int kmaj_swz8(int kr) { return (kr & 7) | (((kr >> 4) & 1) << 3); }
 
 // Waits until at most n LDS operations of this wave are outstanding (n is a
@@ -163,13 +189,13 @@ __device__ __forceinline__ u32x4_t lds_rd128(const lds_t* p) {
 // Half h (k rows 4h.. of each lane group) of the B operand of the 16-column
 // block at n0 for k-step ks, from the k-major layout: a transposing read, 8
 // bytes per lane; valid after a matching lgkm_wait.
-template <Elem E>
+template <Elem E, int BN>
 __device__ __forceinline__ u32x2_t lds_rd_tr(const lds_t* lB, int ks, int n0, int h, int lane) {
   const int g = lane >> 4, j = lane & 15;
   int off;
   if constexpr (ElemInfo<E>::bytes == 2) {
     const int kr = ks * 32 + g * 8 + h * 4 + (j >> 2);
-    off = kr * 512 + (((n0 >> 4) ^ kmaj_swz16(kr)) << 5) + ((j & 3) << 3);
+    off = kr * (BN * 2) + (kmaj_pos16<BN>(n0 >> 4, kr) << 5) + ((j & 3) << 3);
   } else {
     const int kr = ks * 64 + g * 16 + h * 8 + (j >> 1);
     off = kr * 256 + (((n0 >> 4) ^ kmaj_swz8(kr)) << 4) + ((j & 1) << 3);
@@ -220,8 +246,8 @@ __device__ __forceinline__ void read_b_all(BRegs<BT, TS::FN>& b, const lds_t* lB
     if constexpr (BT) {
       b.q[fn] = lds_rd128(lB + row_off(wcol0 + fn * 16 + (lane & 15), ks * 4 + (lane >> 4)));
     } else {
-      b.h[fn][0] = lds_rd_tr<E>(lB, ks, wcol0 + fn * 16, 0, lane);
-      b.h[fn][1] = lds_rd_tr<E>(lB, ks, wcol0 + fn * 16, 1, lane);
+      b.h[fn][0] = lds_rd_tr<E, TS::BN>(lB, ks, wcol0 + fn * 16, 0, lane);
+      b.h[fn][1] = lds_rd_tr<E, TS::BN>(lB, ks, wcol0 + fn * 16, 1, lane);
     }
   }
 }
@@ -253,9 +279,9 @@ __device__ __forceinline__ void wait_vmcnt0() { asm volatile("s_waitcnt vmcnt(0)
 // Main loop over all K stages of all shards. For row-major B, `colmap(c)`
 // gives the global column of tile column c (c a multiple of the 16-byte
 // column block, clamped to the matrix). Every load instruction moves 1 KiB:
-// 8 rows of 128 bytes for A and for B given as (n, k); 2 (16-bit) or 4
-// (8-bit) k rows of 256 columns for row-major B. Each wave issues BM/64 A
-// loads and 4 B loads per stage. The schedule is described at the top.
+// 8 rows of 128 bytes for A and for B given as (n, k); 1 KiB of consecutive
+// k rows of BN columns for row-major B. Each wave issues BM/64 A loads and
+// BN/64 B loads per stage. The schedule is described at the top.
 template <Elem E, bool BT, class TS, class ColMap>
 __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                          int64_t row_last, const BDesc& B, int64_t col0,
@@ -265,8 +291,8 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
   constexpr int KE = kKBytes / ES;        // K values per stage
   constexpr int CE = 16 / ES;             // K values per 16-byte chunk
   constexpr int NA = TS::BM / 64;         // A loads per wave per stage
-  constexpr int NB = 4;                   // B loads per wave per stage
-  constexpr int KRI = ES == 2 ? 2 : 4;    // k rows per row-major B load
+  constexpr int NB = TS::BN / 64;         // B loads per wave per stage
+  static_assert(TS::BN == 256 || (ES == 2 && !BT), "192-column tiles: 16-bit row-major B only");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
@@ -300,9 +326,11 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
       b_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
       b_key[j] = c * CE;
     } else if constexpr (ES == 2) {
-      const int kr = 2 * (NB * wave + j) + (lane >> 5);
-      const int pc = lane & 31;
-      const int ch = ((((pc >> 1) ^ kmaj_swz16(kr))) << 1) | (pc & 1);
+      // 1 KiB per load, written linearly over k rows of BN * 2 bytes
+      const int o = (NB * wave + j) * 1024 + 16 * lane;
+      const int kr = o / (TS::BN * 2);
+      const int pc = (o - kr * (TS::BN * 2)) >> 4;
+      const int ch = (kmaj_unpos16<TS::BN>(pc >> 1, kr) << 1) | (pc & 1);
       b_off[j] = static_cast<uint32_t>(kr * B.ld + colmap(ch * 8) * 2);
       b_key[j] = kr;
     } else {
@@ -343,7 +371,7 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
             b_key[jb] < s.kleft ? b_off[jb] : kOffNone);
     } else {
       const int jb = j - NA;
-      dma16(s.rb, s.st + TS::kABytes + KRI * (NB * wave + jb) * (TS::BN * ES),
+      dma16(s.rb, s.st + TS::kABytes + (NB * wave + jb) * 1024,
             b_key[jb] < s.kleft ? b_off[jb] : kOffNone);
     }
   };

@@ -186,7 +186,8 @@ static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s
 }
 
 // Instantiated combinations: F16 -> {F16, F32}; BF16 -> {BF16, F32};
-// I8 -> {BF16, F16, F32, I32}.
+// I8 -> {BF16, F16, F32, I32} (not with 192-column tiles, which take 16-bit
+// row-major B only).
 template <bool BT, class TS>
 static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArgs& a, int blocks,
                                    hipStream_t s) {
@@ -196,19 +197,22 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   if (in_dtype == MC2_BF16)
     return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
                                 : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
-  switch (out_dtype) {
-    case MC2_BF16: return launch_chunked<Elem::I8, BT, TS, Out::BF16>(a, blocks, s);
-    case MC2_F16: return launch_chunked<Elem::I8, BT, TS, Out::F16>(a, blocks, s);
-    case MC2_F32: return launch_chunked<Elem::I8, BT, TS, Out::F32>(a, blocks, s);
-    default: return launch_chunked<Elem::I8, BT, TS, Out::I32>(a, blocks, s);
+  if constexpr (TS::BN != 256) {
+    return hipErrorInvalidValue;
+  } else {
+    switch (out_dtype) {
+      case MC2_BF16: return launch_chunked<Elem::I8, BT, TS, Out::BF16>(a, blocks, s);
+      case MC2_F16: return launch_chunked<Elem::I8, BT, TS, Out::F16>(a, blocks, s);
+      case MC2_F32: return launch_chunked<Elem::I8, BT, TS, Out::F32>(a, blocks, s);
+      default: return launch_chunked<Elem::I8, BT, TS, Out::I32>(a, blocks, s);
+    }
   }
 }
 
-// Tile height for a problem, from the dispatch rounds each choice needs
-// (one workgroup per CU at a time). A 128-row tile costs about 3/4 of a
-// 256-row one (measured on the 8192 x 3072 x 3072 share), so costs are
-// counted in quarter rounds of 256-row tiles; a last 256-row round that is
-// at most half full runs as half tiles (3/4 of a round).
+// Whether a last dispatch round (one workgroup per CU at a time) of 256-row
+// tiles is at most half full: it then runs as 128-row half tiles. A 128-row
+// tile costs about 3/4 of a 256-row one (measured on the 8192 x 3072 x 3072
+// share), so such a round costs 3/4 of a round.
 static bool half_tail(int64_t tiles, int64_t cus) {
   const int64_t rem = tiles % cus;
   return rem > 0 && tiles > rem && 2 * rem <= cus;
@@ -220,14 +224,26 @@ static int64_t chunk_tiles(int64_t sq, int sr, int sub, int bm, int64_t tn) {
   return (sr * ((sq + bm) / bm) + (sub - sr) * ((sq + bm - 1) / bm)) * tn;
 }
 
-static bool use_tall_tiles(int64_t sq, int sr, int sub, int64_t n, int W) {
+// Tile shape for a problem: 0 = 256 x 256 (a last round at most half full
+// runs as 128-row halves), 1 = 128 x 256, 2 = 256 x 192 (16-bit inputs with
+// row-major B only). Costs are counted in quarter rounds of 256 x 256 tiles;
+// a 128 x 256 or a 256 x 192 tile counts 3. A 256 x 192 tile is taken only
+// where its rounds are cheaper than both others (8192 x 3072 on 256 CUs: 512
+// tiles in 2 rounds, against 384 whole tiles in 1.5 rounds).
+static int tile_shape(int64_t sq, int sr, int sub, int64_t n, int W, bool narrow_ok) {
   const int64_t cus = num_cus();
   const int64_t tn = (n + 255) / 256;
   const int64_t tl = chunk_tiles(sq, sr, sub, 256, tn) * W;
   const int64_t tm = chunk_tiles(sq, sr, sub, 128, tn) * W;
   const int64_t rl = (tl + cus - 1) / cus, rm = (tm + cus - 1) / cus;
   const int64_t cost_l = half_tail(tl, cus) ? 4 * (rl - 1) + 3 : 4 * rl;
-  return cost_l <= 3 * rm;
+  const int64_t cost_m = 3 * rm;
+  if (narrow_ok) {
+    const int64_t tnn = chunk_tiles(sq, sr, sub, 256, (n + 191) / 192) * W;
+    const int64_t cost_n = 3 * ((tnn + cus - 1) / cus);
+    if (cost_n < cost_l && cost_n < cost_m) return 2;
+  }
+  return cost_l <= cost_m ? 0 : 1;
 }
 
 int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n, int W,
@@ -261,11 +277,13 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   a.sub = sub;
   a.sq = a.mc / sub;
   a.sr = static_cast<int>(a.mc % sub);
-  const bool tall = use_tall_tiles(a.sq, a.sr, sub, n, W);
+  const int shape = tile_shape(a.sq, a.sr, sub, n, W, es == 2 && !x2_trans);
+  const bool tall = shape != 1;
   const int BM = tall ? TileL::BM : TileM::BM;
+  const int BN = shape == 2 ? TileN::BN : TileL::BN;
   a.tiles_m1 = static_cast<int>((a.sq + BM) / BM);
   a.tiles_m0 = static_cast<int>((a.sq + BM - 1) / BM);
-  a.tiles_n = static_cast<int>((n + 255) / 256);
+  a.tiles_n = static_cast<int>((n + BN - 1) / BN);
   a.tiles_long = a.tiles_m1 * a.tiles_n;
   a.tiles_short = a.tiles_m0 * a.tiles_n;
   const int64_t per_chunk = chunk_tiles(a.sq, a.sr, sub, BM, a.tiles_n);
@@ -289,13 +307,15 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   // A last round filled to at most half runs as half tiles (see the kernel).
   int64_t blocks = tiles;
   a.n_full = static_cast<int>(tiles);
-  if (tall && half_tail(tiles, num_cus())) {
+  if (shape == 0 && half_tail(tiles, num_cus())) {
     const int64_t rem = tiles % num_cus();
     a.n_full = static_cast<int>(tiles - rem);
     blocks = tiles + rem;
   }
   hipError_t e;
-  if (tall)
+  if (shape == 2)
+    e = dispatch_chunked<false, TileN>(in_dtype, out_dtype, a, (int)blocks, stream);
+  else if (tall)
     e = x2_trans ? dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)
                  : dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
   else

@@ -189,6 +189,33 @@ def test_last_round_as_half_tiles():
     assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "ag_mm")
 
 
+@pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
+def test_192_column_tiles_full_rounds(dtype):
+    """Shapes whose 256 x 192 tiles fill whole dispatch rounds on 256 CUs, as
+    the 8192 x 3072 share's do: W = 8 chunks of 1000 rows (ragged 256-row
+    tiles), n = 1400 (a last tile of 56 columns), k = 776 (a K tail). Every
+    element against the oracle, with ready flags, in reduce-scatter and
+    AllGatherMatmul order; then the simulated W = 2 reduce-scatter of two
+    shards of k = 392 (chunks of 4000 rows, again 256 tiles)."""
+    W = 8
+    t = "bf16" if dtype == wl.BF16 else None
+    d = wl.gemm_inputs(29, W * 1000, 776, 1400, dtype, std=1.0)
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
+    ref = _oracle_rs(d, W)
+    out = _run_rs(d, W, 3, flags=(flags, counters), epoch=4)
+    assert flags.cpu().tolist() == [4] * W
+    assert counters.cpu().tolist() == [0] * W
+    assert_tol(to_f64(out), ref, f"rs {dtype}")
+    out = mc2.mc2_ag_mm_local(to_dev(d["x1"], t), to_dev(d["x2"], t), W, 5,
+                              ready_flags=flags, flag_counters=counters, epoch=6)
+    torch.cuda.synchronize()
+    assert flags.cpu().tolist() == [6] * W
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype=dtype), "ag_mm")
+    d2 = wl.gemm_inputs(30, 8000, 392, 1400, dtype, std=1.0, nsim=2)
+    assert_tol(to_f64(_run_rs(d2, 2, 0)), _oracle_rs(d2, 2), f"sim rs {dtype}")
+
+
 # ------------------------------------------------- AllGatherMatmul input flags
 
 def _hip():
