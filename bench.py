@@ -1,9 +1,11 @@
 """Throughput of the MC2 compute core on one MI355X.
 
 Headline step: the AllGatherMatmul local share in bf16 -- gathered x of W=8
-chunks of (1024, 3072) = (8192, 3072) @ (3072, 3072), chunks computed in
+chunks of (1024, 3072) = (8192, 3072) @ weight (3072, 3072), chunks computed in
 rank order with per-chunk ready flags -- reported as TFLOP/s of the rank-chunked
-GEMM kernel. The same JSON line carries the other hot-path rows measured the
+GEMM kernel. The weight is held as an (n, k) Linear weight and passed
+transposed (x2_trans), which the operator's x2 argument allows; the same
+products with x2 given (k, n) are reported as the *_x2_kn rows. The same JSON line carries the other hot-path rows measured the
 same way (int8 quantized MatmulReduceScatter, the MoE expert-parallel local
 path, the large AllGatherMatmul and the simulated W=8 MatmulReduceScatter),
 the roofline of the dominant kernel and the CPU oracle timed on a bounded
@@ -43,6 +45,8 @@ KERNEL_SOURCES = ["gemm_collective_core_amd/csrc/gemm_core.hpp",
                   "gemm_collective_core_amd/csrc/mc2_common.hpp",
                   "gemm_collective_core_amd/csrc/mc2_host.hpp"]
 TRAFFIC_FILE = "profiles/traffic_ag_mm_bf16_8192x3072x3072.json"
+# The headline launch the recorded traffic must belong to.
+HEADLINE_LAUNCH = "ag_mm bf16 8192x3072x3072 W=8 rank 0, x2 (n, k) with x2_trans, ready flags"
 
 
 def kernel_source_hash():
@@ -62,13 +66,14 @@ def kernel_source_hash():
 
 def recorded_traffic():
     """HBM bytes per launch of the headline kernel from the committed counter
-    summary, or None when it is missing or the kernel changed since."""
+    summary, or None when it is missing, the kernel changed since, or it was
+    taken on another launch configuration."""
     path = os.path.join(ROOT, TRAFFIC_FILE)
     if not os.path.exists(path):
         return None
     with open(path, encoding="utf-8") as f:
         rec = json.load(f)
-    if rec.get("source_sha256") != kernel_source_hash():
+    if rec.get("source_sha256") != kernel_source_hash() or rec.get("launch") != HEADLINE_LAUNCH:
         return None
     return rec.get("traffic_bytes_per_launch")
 
@@ -141,7 +146,8 @@ def main():
     if only in ("all", "c2"):
         log("C2: generating inputs")
         d = wl.c2_inputs()
-        x, w = to_dev(d["x1"], True), to_dev(d["x2"], True)
+        # the weight held as an (n, k) Linear weight and passed transposed
+        x, w = to_dev(d["x1"], True), to_dev(wl.x2_as_nk(d)["x2"], True)
         W = 8
         out = torch.empty((8192, 3072), dtype=torch.bfloat16, device=dev)
         flags = torch.zeros(W, dtype=torch.int32, device=dev)
@@ -150,8 +156,8 @@ def main():
 
         def step():
             ep[0] += 1
-            mc2.mc2_ag_mm_local(x, w, W, 0, out=out, ready_flags=flags, flag_counters=cnt,
-                                epoch=ep[0])
+            mc2.mc2_ag_mm_local(x, w, W, 0, x2_trans=True, out=out, ready_flags=flags,
+                                flag_counters=cnt, epoch=ep[0])
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
@@ -176,30 +182,43 @@ def main():
         inf = torch.full((W,), 1, dtype=torch.int32, device=dev)
         err = torch.zeros(1, dtype=torch.int32, device=dev)
         ms_w = timed(lambda: mc2.mc2_ag_mm_local_inflags(
-            x, w, W, 0, inf, 1, out=out, ready_flags=flags, flag_counters=cnt, epoch=1,
-            dev_err=err), 200, 20)
+            x, w, W, 0, inf, 1, x2_trans=True, out=out, ready_flags=flags, flag_counters=cnt,
+            epoch=1, dev_err=err), 200, 20)
         assert err.item() == 0
         rows["c2_ag_mm_bf16_inflags"] = {"ms": ms_w, "TFLOP/s": flop / ms_w / 1e9,
                                          "frac_peak": flop / ms_w / 1e9 / PEAK_BF16}
         log(f"C2 with input flags: {ms_w * 1e3:.1f} us  {flop / ms_w / 1e9:.1f} TFLOP/s")
+        # the same launch with x2 given (k, n)
+        del w
+        w = to_dev(d["x2"], True)
+        ms_kn = timed(lambda: mc2.mc2_ag_mm_local(x, w, W, 0, out=out, ready_flags=flags,
+                                                  flag_counters=cnt, epoch=2), 200, 20)
+        rows["c2_ag_mm_bf16_x2_kn"] = {"ms": ms_kn, "TFLOP/s": flop / ms_kn / 1e9,
+                                       "frac_peak": flop / ms_kn / 1e9 / PEAK_BF16}
+        log(f"C2 with x2 given (k, n): {ms_kn * 1e3:.1f} us  {flop / ms_kn / 1e9:.1f} TFLOP/s")
         del x, w, out
 
     # ---------------------------------------------------------------- C3
     if only in ("all", "c3"):
         log("C3: generating inputs")
         d = wl.c3_inputs()
-        x1, x2 = to_dev(d["x1"]), to_dev(d["x2"])
         s1, s2 = to_dev(d["x1_scale"]), to_dev(d["x2_scale"])
         out = torch.empty((4096, 2048), dtype=torch.bfloat16, device=dev)
         flags = torch.zeros(4, dtype=torch.int32, device=dev)
         cnt = torch.zeros(4, dtype=torch.int32, device=dev)
-        ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, 4, 0, x1_scale=s1, x2_scale=s2, out=out,
-                                               ready_flags=flags, flag_counters=cnt, epoch=1),
-                   1000, 50)
-        top = 2.0 * 4096 * 8192 * 2048 / ms / 1e9
-        rows["c3_mm_rs_int8"] = {"ms": ms, "TOP/s": top, "frac_peak": top / PEAK_I8}
-        log(f"C3 int8 MM-RS: {ms * 1e3:.1f} us  {top:.1f} TOP/s  ({100 * top / PEAK_I8:.1f}% of peak)")
-        del x1, x2, out
+        x1 = to_dev(d["x1"])
+        # x2 as a transposed (n, k) weight (the row), then given (k, n)
+        for name, dd in (("c3_mm_rs_int8", wl.x2_as_nk(d)), ("c3_mm_rs_int8_x2_kn", d)):
+            x2 = to_dev(dd["x2"])
+            ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, 4, 0, x2_trans=dd["x2_trans"],
+                                                   x1_scale=s1, x2_scale=s2, out=out,
+                                                   ready_flags=flags, flag_counters=cnt, epoch=1),
+                       1000, 50)
+            top = 2.0 * 4096 * 8192 * 2048 / ms / 1e9
+            rows[name] = {"ms": ms, "TOP/s": top, "frac_peak": top / PEAK_I8}
+            log(f"{name}: {ms * 1e3:.1f} us  {top:.1f} TOP/s  ({100 * top / PEAK_I8:.1f}% of peak)")
+            del x2
+        del x1, out
 
     # ---------------------------------------------------------------- C4
     if only in ("all", "c4"):
@@ -322,23 +341,38 @@ def main():
         a, b = wl.c5_inputs()
         W = 8
         if only in ("all", "c5a"):
-            x, w = to_dev(a["x1"], True), to_dev(a["x2"], True)
+            x = to_dev(a["x1"], True)
             out = torch.empty((16384, 3584), dtype=torch.bfloat16, device=dev)
             flags = torch.zeros(W, dtype=torch.int32, device=dev)
             cnt = torch.zeros(W, dtype=torch.int32, device=dev)
-            ms = timed(lambda: mc2.mc2_ag_mm_local(x, w, W, 0, out=out, ready_flags=flags,
-                                                   flag_counters=cnt, epoch=1), 100, 10)
-            tf = 2.0 * 16384 * 8192 * 3584 / ms / 1e9
-            rows["c5a_ag_mm_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
-            log(f"C5a AG-MM: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
-            del x, w, out
+            # x2 as a transposed (n, k) weight (the row), then given (k, n)
+            for name, aa in (("c5a_ag_mm_bf16", wl.x2_as_nk(a)), ("c5a_ag_mm_bf16_x2_kn", a)):
+                w = to_dev(aa["x2"], True)
+                ms = timed(lambda: mc2.mc2_ag_mm_local(x, w, W, 0, x2_trans=aa["x2_trans"],
+                                                       out=out, ready_flags=flags,
+                                                       flag_counters=cnt, epoch=1), 100, 10)
+                tf = 2.0 * 16384 * 8192 * 3584 / ms / 1e9
+                rows[name] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+                log(f"{name}: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
+                del w
+            del x, out
         if only in ("all", "c5b"):
-            x1, x2 = to_dev(b["x1"], True), to_dev(b["x2"], True)
+            x1 = to_dev(b["x1"], True)
             out = torch.empty((16384, 8192), dtype=torch.bfloat16, device=dev)
             flags = torch.zeros(W, dtype=torch.int32, device=dev)
             cnt = torch.zeros(W, dtype=torch.int32, device=dev)
+            x2 = to_dev(b["x2"], True)
             ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, W, 0, out=out, ready_flags=flags,
                                                    flag_counters=cnt, epoch=1), 50, 5)
+            tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
+            rows["c5b_sim_rs_bf16_x2_kn"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
+            log(f"C5b sim-W=8 MM-RS, x2 given (k, n): {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
+            # the row and everything after it: x2 shards as transposed (n, k) weights
+            del x2
+            x2 = to_dev(wl.x2_as_nk(b)["x2"], True)
+            ms = timed(lambda: mc2.mc2_mm_rs_local(x1, x2, W, 0, x2_trans=True, out=out,
+                                                   ready_flags=flags, flag_counters=cnt, epoch=1),
+                       50, 5)
             tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
             rows["c5b_sim_rs_bf16"] = {"ms": ms, "TFLOP/s": tf, "frac_peak": tf / PEAK_BF16}
             log(f"C5b sim-W=8 MM-RS: {ms * 1e3:.1f} us  {tf:.1f} TFLOP/s")
@@ -348,8 +382,8 @@ def main():
                              dtype=torch.uint8, device=dev)
             for mode, name in ((mc2.MC2_AR_ONE_ROUNDING, "one"), (mc2.MC2_AR_RANK_ROUNDED, "rank"),
                                (mc2.MC2_AR_HOP_ROUNDED, "hop")):
-                ms = timed(lambda: mc2.mc2_mm_ar_local(x1, x2, W, rounding=mode, out=out,
-                                                       workspace=ws), 30, 3)
+                ms = timed(lambda: mc2.mc2_mm_ar_local(x1, x2, W, rounding=mode, x2_trans=True,
+                                                       out=out, workspace=ws), 30, 3)
                 tf = 2.0 * 8 * 16384 * 1024 * 8192 / ms / 1e9
                 rows[f"c5b_mm_ar_{name}_rounding_bf16"] = {"ms": ms, "TFLOP/s": tf,
                                                            "frac_peak": tf / PEAK_BF16}
@@ -393,14 +427,16 @@ def main():
         W = 8
         cases = {
             "c2_ag_mm": (lambda S, out, fl, cn, e: mc2.mc2_ag_mm_local(
-                xc2, wc2, W, 0, out=out, ready_flags=fl, flag_counters=cn, epoch=e, comm_turn=S),
+                xc2, wc2, W, 0, x2_trans=True, out=out, ready_flags=fl, flag_counters=cn, epoch=e,
+                comm_turn=S),
                 (8192, 3072), 2.0 * 8192 * 3072 * 3072, 200),
             "c5b_sim_rs": (lambda S, out, fl, cn, e: mc2.mc2_mm_rs_local(
-                x1b, x2b, W, 0, out=out, ready_flags=fl, flag_counters=cn, epoch=e, comm_turn=S),
+                x1b, x2b, W, 0, x2_trans=True, out=out, ready_flags=fl, flag_counters=cn, epoch=e,
+                comm_turn=S),
                 (16384, 8192), 2.0 * 8 * 16384 * 1024 * 8192, 30),
         }
-        xc2, wc2 = to_dev(d["x1"], True), to_dev(d["x2"], True)
-        x1b, x2b = to_dev(b["x1"], True), to_dev(b["x2"], True)
+        xc2, wc2 = to_dev(d["x1"], True), to_dev(wl.x2_as_nk(d)["x2"], True)
+        x1b, x2b = to_dev(b["x1"], True), to_dev(wl.x2_as_nk(b)["x2"], True)
         split = {}
         for name, (call, shape, flop, iters) in cases.items():
             out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
@@ -466,9 +502,11 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0, 0.02) bf16 inputs resident in HBM)",
         "config": {"workload": "AllGatherMatmul local share: gathered x of W=8 chunks "
-                               "(8192, 3072) @ (3072, 3072) bf16, fp32 accumulation, chunks in "
-                               "rank order from rank 0, per-chunk ready flags",
-                   "world_size": 8, "m": 8192, "k": 3072, "n": 3072},
+                               "(8192, 3072) @ weight (3072, 3072) bf16, the weight held as an "
+                               "(n, k) Linear weight and passed transposed (x2_trans), fp32 "
+                               "accumulation, chunks in rank order from rank 0, per-chunk ready "
+                               "flags; rows c2_ag_mm_bf16_x2_kn and *_x2_kn time x2 given (k, n)",
+                   "world_size": 8, "m": 8192, "k": 3072, "n": 3072, "x2_layout": "(n, k), x2_trans"},
         "roofline": {"bound": "mfma", "achieved": headline["tflops"], "peak": PEAK_BF16,
                      "unit": "TFLOP/s", "frac": headline["tflops"] / PEAK_BF16,
                      "traffic": recorded_traffic()},

@@ -154,6 +154,17 @@ def c5_inputs(seed=1005, m=16384, k_a=8192, n_a=3584, world_size=8,
     return a, b
 
 
+def x2_as_nk(d):
+    """The same GEMM inputs with x2 held as (n, k) (stacked (nsim, n, k)) and
+    flagged x2_trans: the layout of a Linear weight that is passed to the
+    operator transposed. Same values, only the storage order changes."""
+    out = dict(d)
+    x2 = np.asarray(d["x2"])
+    out["x2"] = np.ascontiguousarray(np.swapaxes(x2, -1, -2))
+    out["x2_trans"] = True
+    return out
+
+
 # --------------------------------------------------------------------------
 # MoE expert-parallel workloads
 # --------------------------------------------------------------------------
