@@ -1,8 +1,8 @@
 // Device building blocks of the MFMA contraction kernels (gfx950).
 //
 // Workgroup: 8 waves = 512 threads, two waves per SIMD, computing a BM x BN
-// output tile (256 x 256 or 128 x 256); wave (wm, wn) owns a WTM x WTN
-// sub-tile. Two waves per SIMD let one wave's MFMAs run while the other waits
+// output tile (256 x 256, 128 x 256, or 256 x 192 for 16-bit inputs); wave
+// (wm, wn) owns a WTM x WTN sub-tile. Two waves per SIMD let one wave's MFMAs run while the other waits
 // on its operand reads or on a load instruction the memory pipeline has not
 // yet taken.
 //
@@ -48,8 +48,9 @@
 //    i mod 8 of the pieces read by lanes 2e + i/8 (e = 0..7). So lane j reads
 //    k row 4h + (j >> 2), columns 4(j & 3).. (16-bit) or k row 8h + (j >> 1),
 //    columns 8(j & 1).. (8-bit), and lane i receives consecutive k values of
-//    column i. Rows are swizzled in 32-byte pairs (16-bit) or 16-byte chunks
-//    (8-bit) so that the rows one read touches sit on distinct banks.
+//    column i. Rows are swizzled in 32-byte pairs (16-bit; XOR for 512-byte
+//    rows, a rotation for the 384-byte rows of 192-column tiles) or 16-byte
+//    chunks (8-bit) so that the rows one read touches sit on distinct banks.
 #pragma once
 
 #include <type_traits>

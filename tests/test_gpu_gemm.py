@@ -216,6 +216,40 @@ def test_192_column_tiles_full_rounds(dtype):
     assert_tol(to_f64(_run_rs(d2, 2, 0)), _oracle_rs(d2, 2), f"sim rs {dtype}")
 
 
+def test_192_column_tiles_other_paths():
+    """Other paths of a 192-column-tile launch (all three shapes select them on
+    256 CUs): bias with the test-only fp32 output; comm_turn 3 pieces with
+    their own flags, bit-identical to the unsplit call (W = 2 chunks of 3000
+    rows, pieces of 1000); input flags, all present."""
+    W = 8
+    d = wl.gemm_inputs(31, W * 1000, 392, 1400, wl.BF16, std=1.0, bias=True)
+    out = _run_rs(d, W, 2, out_dtype="f32", bias=d["bias"])
+    assert_tol(to_f64(out), _oracle_rs(d, W, out_dtype="f32", bias=d["bias"]), "bias f32",
+               rtol=1e-4, atol=1e-3)
+    d2 = wl.gemm_inputs(32, 6000, 392, 1400, wl.BF16, std=1.0)
+    x1, x2 = to_dev(d2["x1"], "bf16"), to_dev(d2["x2"], "bf16")
+    base = mc2.mc2_mm_rs_local(x1, x2, 2, 1)
+    flags = torch.zeros(6, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(6, dtype=torch.int32, device="cuda")
+    out = mc2.mc2_mm_rs_local(x1, x2, 2, 1, ready_flags=flags, flag_counters=cnt, epoch=7,
+                              comm_turn=3)
+    torch.cuda.synchronize()
+    assert torch.equal(out, base)
+    assert flags.cpu().tolist() == [7] * 6 and cnt.cpu().tolist() == [0] * 6
+    assert_tol(to_f64(base), _oracle_rs(d2, 2), "unsplit")
+    inf = torch.full((W,), 5, dtype=torch.int32, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
+    cnt = torch.zeros(W, dtype=torch.int32, device="cuda")
+    out = mc2.mc2_ag_mm_local_inflags(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 6,
+                                      inf, 5, ready_flags=flags, flag_counters=cnt, epoch=9,
+                                      dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    assert flags.cpu().tolist() == [9] * W and cnt.cpu().tolist() == [0] * W
+    assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "inflags")
+
+
 # ------------------------------------------------- AllGatherMatmul input flags
 
 def _hip():
