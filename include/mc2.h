@@ -82,6 +82,10 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
  *
  *   x1      (nsim, m, k) in_dtype             x2  (nsim, k, n), or (nsim, n, k)
  *                                                 when x2_trans != 0
+ *           x2_trans is the page's transposed x2 (x2 may be passed transposed,
+ *           the input may not): a Linear weight held (n, k). It is the faster
+ *           layout here, since each x2 operand is one 16-byte LDS read instead
+ *           of two transposing 8-byte reads.
  *   in_dtype MC2_F16, MC2_BF16 or MC2_I8 (x1 and x2 share it)
  *   bias    NULL or (n): in_dtype for F16/BF16 inputs; BF16 for I8 inputs
  *           (an extension: the page allows only a float bias of the input's
