@@ -352,26 +352,37 @@ struct TransposeArgs {
 // PT[c][pstart[g] + i] = P[base + gstart[g] + i][c] for every local group g
 // and row i < count g, and zeros in the columns after each group up to the next
 // multiple of 64, so that a 16-byte K piece read past the group's last row
-// holds zeros. Workgroup x takes a 64-row block of one group (blocks start at
-// the group's first row, so the block's destination columns start on a
-// 128-byte line) and walks over the columns in 64-column tiles, each through
-// LDS: 16-byte loads along the rows, then every thread gathers 8 rows of one
-// column and writes them with one 16-byte store. The grid may have more
-// blocks than the groups need (the host knows only a bound); the rest exit.
+// holds zeros. The work is cut into items: a 64-row block of one group (blocks
+// start at the group's first row, so the block's destination columns start on
+// a 128-byte line) times a 256-column tile. The grid holds as many workgroups
+// as fit on the chip at once, and workgroup x takes items x, x + grid, ...
+// (the host knows only a bound on the row blocks; the kernel counts them).
+// An item goes through one of two LDS buffers:
+// - every thread loads four 16-byte pieces along the rows and writes them to
+//   LDS, where 8-byte unit u of row r sits at unit u ^ 4 ((r / 8) ^ (r mod 8));
+// - every thread then reads 8 rows x 4 columns (eight 8-byte reads) and writes
+//   the 4 columns, 8 rows each, with 16-byte stores.
+// The swizzle puts the 16-byte writes of a quarter wave, the 8-byte reads of
+// a half wave at one row offset, and the 8 rows one lane reads (which the
+// compiler may pair into one instruction) on distinct banks. With two buffers
+// one barrier per item suffices: a buffer is written again only after every
+// thread has passed the following item's barrier, so has finished reading it.
+// The next item's loads are issued after the current item's stores, so that
+// waiting for them also covers the stores.
+constexpr int kTrCols = 256;  // columns per item; LDS rows of 512 bytes
+
 __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
   __shared__ GroupTable t;
   __shared__ int64_t s_bstart[kMaxLocalExperts + 1];
-  constexpr int pitch = 132;  // bytes per LDS row: 64 bf16 + 4, so column reads are conflict-free
-  __shared__ __attribute__((aligned(16))) char tile_raw[64 * pitch];
-  lds_t* tile = (lds_t*)tile_raw;
-  if (blockIdx.x == 0 && blockIdx.y == 0)
+  __shared__ __attribute__((aligned(16))) char tile_raw[2][64 * kTrCols * 2];
+  if (blockIdx.x == 0)
     for (int64_t i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero[i] = 0u;
   load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
   const int El = p.local_experts;
   const int64_t n = t.gstart[El];
   const int64_t base = p.at_send ? t.base : 0;
   if (t.bad || base + n > p.p_cap || t.pstart[El] > p.kt) {
-    if (threadIdx.x == 0 && blockIdx.x == 0 && blockIdx.y == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
+    if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
     return;
   }
   if (threadIdx.x == 0) {
@@ -383,43 +394,76 @@ __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
     s_bstart[El] = b;
   }
   __syncthreads();
-  const int64_t blk = blockIdx.x;
-  if (blk >= s_bstart[El]) return;
-  int g = 0;
-  while (g + 1 < El && s_bstart[g + 1] <= blk) ++g;
-  const int64_t j64 = (blk - s_bstart[g]) * 64;       // first row of the block within group g
-  const int64_t nr = t.cnt[g] - j64 < 64 ? t.cnt[g] - j64 : 64;
-  const int64_t src0 = base + t.gstart[g] + j64;      // first source row
-  const int64_t dst0 = t.pstart[g] + j64;             // first destination column (64-aligned)
-  const int tid = threadIdx.x;
-  const int lr = tid >> 3, ch = tid & 7;              // load: row, 16-byte chunk
-  const int oc = tid >> 3, r8 = (tid & 7) * 8;        // store: column, first of 8 rows
-  for (int64_t c0 = static_cast<int64_t>(blockIdx.y) * 64; c0 < p.cols; c0 += 64 * gridDim.y) {
-    {
-      const int64_t gc = c0 + ch * 8;
-      u32x4_t v = zero_v4();
-      if (lr < nr && gc < p.cols)
-        v = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(p.P + (src0 + lr) * p.ldp + gc * 2));
+  const int64_t ctiles = (p.cols + kTrCols - 1) / kTrCols;
+  const int64_t items = s_bstart[El] * ctiles;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int lr = tid >> 5, ch = tid & 31;             // load: rows lr + 16 l, 16-byte piece ch
+  const int rg = lane & 7;                            // store: rows 8 rg .. 8 rg + 7,
+  const int cg = (tid >> 6) * 8 + (lane >> 3);        // columns 4 cg .. 4 cg + 3
+  const int pu = cg ^ (4 * rg);                       // their 8-byte unit in LDS, before the row term
+  struct Item {
+    int64_t c0, nr, src0, dst0;
+  };
+  auto locate = [&](int64_t it) {
+    const int64_t blk = it / ctiles;
+    int g = 0;
+    while (g + 1 < El && s_bstart[g + 1] <= blk) ++g;
+    const int64_t j64 = (blk - s_bstart[g]) * 64;     // first row of the block within group g
+    Item m;
+    m.c0 = (it - blk * ctiles) * kTrCols;
+    m.nr = t.cnt[g] - j64 < 64 ? t.cnt[g] - j64 : 64;
+    m.src0 = base + t.gstart[g] + j64;                // first source row
+    m.dst0 = t.pstart[g] + j64;                       // first destination column (64-aligned)
+    return m;
+  };
+  u32x4_t v[4];
+  auto load = [&](const Item& m) {
+    const int64_t gc = m.c0 + ch * 8;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        *reinterpret_cast<MC2_LDS uint32_t*>(tile + lr * pitch + ch * 16 + j * 4) = v[j];
+    for (int l = 0; l < 4; ++l) {
+      const int r = lr + 16 * l;
+      v[l] = zero_v4();
+      if (r < m.nr && gc < p.cols)
+        v[l] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(p.P + (m.src0 + r) * p.ldp + gc * 2));
+    }
+  };
+  int64_t it = blockIdx.x;
+  if (it >= items) return;
+  Item cur = locate(it);
+  load(cur);
+  for (int buf = 0; it < items; it += gridDim.x, buf ^= 1) {
+    lds_t* tb = (lds_t*)tile_raw[buf];
+#pragma unroll
+    for (int l = 0; l < 4; ++l) {
+      const int r = lr + 16 * l;
+      *reinterpret_cast<MC2_LDS u32x4_t*>(tb + r * (kTrCols * 2) + ((ch ^ (2 * ((r >> 3) ^ (r & 7)))) << 4)) = v[l];
     }
     __syncthreads();
-    if (c0 + oc < p.cols) {
-      u32x4_t w;
+    const Item m = cur;
+    if (m.c0 + 4 * cg < p.cols) {
+      uint64_t w[8];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t lo = *reinterpret_cast<const MC2_LDS uint16_t*>(tile + (r8 + 2 * j) * pitch + oc * 2);
-        const uint32_t hi =
-            *reinterpret_cast<const MC2_LDS uint16_t*>(tile + (r8 + 2 * j + 1) * pitch + oc * 2);
-        w[j] = lo | (hi << 16);
+      for (int i = 0; i < 8; ++i)
+        w[i] = *reinterpret_cast<const MC2_LDS uint64_t*>(tb + (8 * rg + i) * (kTrCols * 2) + (pu ^ (4 * i)) * 8);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4_t o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = static_cast<uint32_t>(w[2 * j] >> (16 * q)) & 0xffffu;
+          const uint32_t hi = static_cast<uint32_t>(w[2 * j + 1] >> (16 * q)) & 0xffffu;
+          o[j] = lo | (hi << 16);
+        }
+        // rows past the group's end were loaded as zeros: they pad the group
+        __builtin_nontemporal_store(
+            o, reinterpret_cast<u32x4_t*>(p.PT + ((m.c0 + 4 * cg + q) * p.kt + m.dst0 + 8 * rg) * 2));
       }
-      // rows past the group's end were loaded as zeros: they pad the group
-      __builtin_nontemporal_store(
-          w, reinterpret_cast<u32x4_t*>(p.PT + ((c0 + oc) * p.kt + dst0 + r8) * 2));
     }
-    __syncthreads();
+    if (it + gridDim.x < items) {
+      cur = locate(it + gridDim.x);
+      load(cur);
+    }
   }
 }
 
@@ -745,17 +789,15 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   t.dev_err = dev_err;
   t.zero = reinterpret_cast<uint32_t*>(ws + L.off_ctr);
   t.n_zero = per_group * local_experts;
-  // 64-row blocks, each inside one group (at most rows / 64 + E_l of them);
-  // the column tiles are split over a few workgroups only when there are too
-  // few row blocks to fill the chip
+  // items: 64-row blocks, each inside one group (at most rows / 64 + E_l of
+  // them), times 256-column tiles; two workgroups fit on a CU (LDS), and the
+  // grid holds that many, or fewer when there are fewer items
   const int64_t rb = p_cap / 64 + local_experts;
-  int64_t cb = (M + 63) / 64;
-  const int64_t want = (4 * static_cast<int64_t>(num_cus()) + rb - 1) / (rb > 0 ? rb : 1);
-  cb = cb < want ? cb : want;
-  cb = cb < 1 ? 1 : cb;
-  if (rb > 0x7fffffff) return MC2_ERR_SHAPE;
-  hipLaunchKernelGGL(group_transpose_kernel,
-                     dim3(static_cast<unsigned>(rb > 0 ? rb : 1), static_cast<unsigned>(cb)),
+  const int64_t items = rb * ((M + kTrCols - 1) / kTrCols);
+  int64_t gx = 2 * static_cast<int64_t>(num_cus());
+  gx = gx < items ? gx : items;
+  gx = gx < 1 ? 1 : gx;
+  hipLaunchKernelGGL(group_transpose_kernel, dim3(static_cast<unsigned>(gx)),
                      dim3(512), 0, stream, t);
   if (hipGetLastError() != hipSuccess) return MC2_ERR_HIP;
   WgradArgs w{};
