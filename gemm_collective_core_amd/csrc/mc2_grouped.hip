@@ -577,11 +577,15 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
                                   col0, cm, ks, acc);
   if (nslices == 1) {
+    // non-temporal: the result is not read again here (measured: 1-2% faster
+    // than plain stores; the same hint on the split slices' partials, which
+    // the last slice reads back, was slower)
     char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
     epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
                                               nullptr, [&](int r, int c, float v) {
                                                 if (r < nrows && c < ncols)
-                                                  put_out_global<Out::F32>(base_out + (r * p.N + c) * 4, v);
+                                                  __builtin_nontemporal_store(
+                                                      v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
                                               });
     return;
   }
