@@ -213,6 +213,38 @@ def test_weight_gradient_split_groups_deterministic():
     _assert_wgrad(outs[0][0], ref_dw1, _dec(b["send"]), _dec(b["dg"]), recv, "split dW1")
 
 
+def test_weight_gradient_many_transpose_items_ragged_columns():
+    """40011 rows in ragged groups with H = 264 (a 256-column tile plus an
+    8-column one) and I = 136: the token-major operands are transposed in
+    more 64-row x 256-column items than the grid has workgroups, so each
+    workgroup walks several items through both LDS buffers, partial column
+    tiles included. The whole dW1 and dW2 against the oracle."""
+    H, I = 264, 136
+    send_counts = np.array([17001, 3, 0, 64, 22943], dtype=np.int32)
+    recv = send_counts.copy()
+    n = int(recv.sum())
+    d = wl.moe_inputs(seed=76, tokens=16, hidden=H, num_experts=5, topk=1, local_experts=5,
+                      inter=I, w_std=0.05)
+    b = wl.moe_backward_inputs(77, n, H, I)
+    dev = {k: to_dev(v, "bf16") for k, v in b.items()}
+    rc, sc = to_dev(recv), to_dev(send_counts)
+    w1, w2 = to_dev(d["w1"], "bf16"), to_dev(d["w2"], "bf16")
+    dx = torch.zeros((n, H), dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    _, dw2 = mc2.mc2_gmm_combine_backward(dev["dy"], rc, sc, w2, dev["h"], ep_rank=0,
+                                          num_experts=5, dev_err=err)
+    _, dw1 = mc2.mc2_gmm_dispatch_backward(dev["dg"], rc, sc, w1, dev["send"], dx, ep_rank=0,
+                                           num_experts=5, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    _, ref_dw2 = om.combine_backward(b["dy"], recv, send_counts, ep_rank=0, local_experts=5,
+                                     w2=d["w2"], h=b["h"], act="none")
+    _assert_wgrad(dw2.cpu().numpy(), ref_dw2, _dec(b["h"]), _dec(b["dy"]), recv, "many-item dW2")
+    _, ref_dw1 = om.dispatch_backward(b["dg"], recv, send_counts, ep_rank=0, local_experts=5,
+                                      w1=d["w1"], send_buf=b["send"], dx_buf=np.zeros((n, H)))
+    _assert_wgrad(dw1.cpu().numpy(), ref_dw1, _dec(b["send"]), _dec(b["dg"]), recv, "many-item dW1")
+
+
 def test_backward_no_local_rows():
     """Every local expert receives no rows: the weight gradients are exact
     zeros and no input-gradient row is written."""
