@@ -400,7 +400,7 @@ __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
   const int lr = tid >> 5, ch = tid & 31;             // load: rows lr + 16 l, 16-byte piece ch
   const int rg = lane & 7;                            // store: rows 8 rg .. 8 rg + 7,
   const int cg = (tid >> 6) * 8 + (lane >> 3);        // columns 4 cg .. 4 cg + 3
-  const int pu = cg ^ (4 * rg);                       // their 8-byte unit in LDS, before the row term
+  const int pu = cg ^ (4 * rg);                       // their LDS unit, less the row term
   struct Item {
     int64_t c0, nr, src0, dst0;
   };
@@ -437,7 +437,8 @@ __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
 #pragma unroll
     for (int l = 0; l < 4; ++l) {
       const int r = lr + 16 * l;
-      *reinterpret_cast<MC2_LDS u32x4_t*>(tb + r * (kTrCols * 2) + ((ch ^ (2 * ((r >> 3) ^ (r & 7)))) << 4)) = v[l];
+      const int pch = ch ^ (2 * ((r >> 3) ^ (r & 7)));  // 16-byte piece: 8-byte units move in pairs
+      *reinterpret_cast<MC2_LDS u32x4_t*>(tb + r * (kTrCols * 2) + (pch << 4)) = v[l];
     }
     __syncthreads();
     const Item m = cur;
@@ -445,7 +446,8 @@ __global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
       uint64_t w[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i)
-        w[i] = *reinterpret_cast<const MC2_LDS uint64_t*>(tb + (8 * rg + i) * (kTrCols * 2) + (pu ^ (4 * i)) * 8);
+        w[i] = *reinterpret_cast<const MC2_LDS uint64_t*>(tb + (8 * rg + i) * (kTrCols * 2) +
+                                                          (pu ^ (4 * i)) * 8);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         u32x4_t o;
@@ -497,11 +499,13 @@ struct WgradArgs {
 // the group, L = kSliceRows; A is the group's column range of the transposed
 // workspace, B the group's rows of Q. Units are numbered group by group, the
 // groups with most rows first (so the longest units are dispatched first and
-// the short ones fill the end of the launch), slice by slice, tile fastest. A group of one slice stores its tile; for a
-// split group every slice stores its partial tile in its slot, and the last
-// slice to finish a tile (counted with an agent-scope release / acquire, as
-// the ready flags) sums the partials in slice order, so the result does not
-// depend on timing. An empty group gets zeros. The grid may have more
+// the short ones fill the end of the launch), slice by slice, tile fastest. A
+// group of one slice stores its tile (non-temporal: the result is not read
+// again here; the same hint on the partials below, which are read back, was
+// slower); for a split group every slice stores its partial tile in its slot,
+// and the last slice to finish a tile (counted with an agent-scope release /
+// acquire, as the ready flags) sums the partials in slice order, so the result
+// does not depend on timing. An empty group gets zeros. The grid may have more
 // workgroups than units (the host knows only a bound); the rest exit.
 template <class TS>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
@@ -577,16 +581,12 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
                                   col0, cm, ks, acc);
   if (nslices == 1) {
-    // non-temporal: the result is not read again here (measured: 1-2% faster
-    // than plain stores; the same hint on the split slices' partials, which
-    // the last slice reads back, was slower)
     char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
-    epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                              nullptr, [&](int r, int c, float v) {
-                                                if (r < nrows && c < ncols)
-                                                  __builtin_nontemporal_store(
-                                                      v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
-                                              });
+    epilogue_linear<Elem::BF16, TS, Out::F32>(
+        acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr, [&](int r, int c, float v) {
+          if (r < nrows && c < ncols)
+            __builtin_nontemporal_store(v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
+        });
     return;
   }
   // split group: this slice's partial tile (dense BM x BN) into its slot
