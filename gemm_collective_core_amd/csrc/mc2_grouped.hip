@@ -234,46 +234,75 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
   // 32x+31 of every round of the tile sequence (see xcd_tile).
   const int g8 = gridDim.x;
   const int64_t tfirst = (g8 % 8 == 0) ? (blockIdx.x & 7) * (g8 >> 3) + (blockIdx.x >> 3) : blockIdx.x;
-  for (int64_t t = tfirst; t < total; t += gridDim.x) {
+  // Tile t of the sequence -> (group, row tile, column tile) for TS::BM-row tiles.
+  struct Place {
+    int g;
+    int64_t tm, tn;
+  };
+  auto place = [&](int64_t t) {
     int g = 0;
     while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
     g = uni(g);
-    const int64_t gs = uni(s_gstart[g]);
-    const int64_t cnt = uni(s_gstart[g + 1]) - gs;
+    const int64_t cnt = uni(s_gstart[g + 1]) - uni(s_gstart[g]);
     const int64_t tiles_m = (cnt + TS::BM - 1) / TS::BM;
     const int64_t lt = t - uni(s_tstart[g]);
     // 64-bit division runs on the vector ALU: its results are made uniform again
-    const int64_t tm = uni(lt % tiles_m), tn = uni(lt / tiles_m);
-    const int64_t arow0 = a_base + gs + tm * TS::BM;
+    return Place{g, uni(lt % tiles_m), uni(lt / tiles_m)};
+  };
+  // One output tile of TSX::BM rows (TS, or its 128-row half) from row r0 of
+  // group g, column tile tn.
+  auto run_tile = [&](auto shape, int g, int64_t r0, int64_t tn) {
+    using TSX = decltype(shape);
+    static_assert(TSX::BN == TS::BN, "column tiles are shared by both shapes");
+    const int64_t gs = uni(s_gstart[g]);
+    const int64_t cnt = uni(s_gstart[g + 1]) - gs;
+    const int64_t arow0 = a_base + gs + r0;
     const int64_t arow_end = a_base + gs + cnt;
-    const int64_t orow0 = o_base + gs + tm * TS::BM;
+    const int64_t orow0 = o_base + gs + r0;
     const int64_t ocol0 = tn * OUTC;
 
-    f32x4_t acc[TS::FM][TS::FN];
+    f32x4_t acc[TSX::FM][TSX::FN];
     BDesc bd{p.B + g * p.b_group, p.ldb, p.n_b};
     if constexpr (GLU) {
       GluCols cm{ocol0, p.inter, p.n_b - 8};
-      mainloop<Elem::BF16, false, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
+      mainloop<Elem::BF16, false, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
     } else {
       PlainCols cm{ocol0, p.n_b - 8};
-      mainloop<Elem::BF16, BT, TS>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks, acc);
+      mainloop<Elem::BF16, BT, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks, acc);
     }
     if constexpr (MODE == kSwigluBwd) {
-      swiglu_bwd_epilogue<TS>(smem, acc, p, orow0, arow_end - arow0, ocol0);
+      swiglu_bwd_epilogue<TSX>(smem, acc, p, orow0, arow_end - arow0, ocol0);
       __syncthreads();
-      continue;
+      return;
     }
     constexpr int pitch = OUTC * 2 + 16;
     if constexpr (GLU)
-      stage_swiglu<TS>(smem, pitch, acc);
+      stage_swiglu<TSX>(smem, pitch, acc);
     else
-      epilogue_linear<Elem::BF16, TS, Out::BF16>(
+      epilogue_linear<Elem::BF16, TSX, Out::BF16>(
           acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
           [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
     __syncthreads();
-    store_staged(smem, pitch, OUTC * 2, TS::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
+    store_staged(smem, pitch, OUTC * 2, TSX::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
                  ocol0 * 2, p.n_out * 2);
     __syncthreads();
+  };
+
+  // All tiles have the same K, so the sequence runs in rounds of one tile per
+  // workgroup. A last round filled to at most half runs as 128-row halves, two
+  // workgroups per tile (consecutive tfirst values, so on one XCD).
+  const int64_t G = gridDim.x;
+  const int64_t rem = total % G;
+  const bool halves = rem > 0 && 2 * rem <= G;
+  const int64_t n_full = halves ? total - rem : total;
+  for (int64_t t = tfirst; t < n_full; t += G) {
+    const Place q = place(t);
+    run_tile(TS{}, q.g, q.tm * TS::BM, q.tn);
+  }
+  if (halves && tfirst < 2 * rem) {
+    const Place q = place(n_full + tfirst / 2);
+    const int64_t r0 = q.tm * TS::BM + (tfirst & 1) * TileHalf<TS>::BM;
+    if (r0 < uni(s_gstart[q.g + 1]) - uni(s_gstart[q.g])) run_tile(TileHalf<TS>{}, q.g, r0, q.tn);
   }
 }
 
