@@ -172,6 +172,10 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (
 
 // Persistent grouped GEMM: every workgroup derives the tile -> (expert, rows,
 // columns) map from the device-side counts, so the host never reads them.
+// rows [0, BM/2) or [BM/2, BM) of a TS tile
+template <class TS>
+using TileHalf = Tile<TS::BM / 2, TS::BN, TS::WM, TS::WN>;
+
 template <class TS, int MODE, bool BT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
   constexpr bool GLU = MODE == kSwiglu;

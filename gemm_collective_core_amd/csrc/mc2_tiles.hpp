@@ -99,8 +99,6 @@ __device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
 using TileL = Tile<256, 256, 2, 4>;  // wave sub-tile 128 x 64
 using TileM = Tile<128, 256, 2, 4>;  // wave sub-tile 64 x 64, for small tile counts
 using TileN = Tile<256, 192, 2, 4>;  // wave sub-tile 128 x 48: tile counts that fill whole rounds
-template <class TS>
-using TileHalf = Tile<TS::BM / 2, TS::BN, TS::WM, TS::WN>;  // rows [0, BM/2) or [BM/2, BM) of a TS tile
 
 inline bool valid_world(int W) { return W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32; }
 
