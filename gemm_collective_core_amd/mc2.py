@@ -48,6 +48,27 @@ def _dev(*ts):
     return next(t for t in ts if t is not None).device
 
 
+def _want(t, name, *, shape=None, dtype=None, dtypes=None, numel=None):
+    """Rejects a tensor whose metadata does not match what the kernel will
+    index: the C library only sees pointers and sizes, so a wrong shape or
+    dtype here would make a kernel read or write past the buffer. None
+    passes (optional arguments)."""
+    if t is None:
+        return
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} must hold {numel} elements, got {t.numel()}")
+
+
+_FLOAT16 = (torch.float16, torch.bfloat16)
+_ERR = dict(dtype=torch.int32, numel=1)
+
+
 def _stream(device):
     return torch.cuda.current_stream(device).cuda_stream
 
@@ -80,8 +101,10 @@ def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_s
                     flag_counters=None, epoch=0, comm_turn=0):
     """MatmulReduceScatter compute share; x1 (m, k) or stacked (nsim, m, k),
     x2 (k, n) / (n, k) or stacked. Returns out (m, n)."""
-    dev = _dev(x1, x2, bias, x1_scale, x2_scale, out, flag_counters)
-    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
+    if x1.dim() not in (2, 3):
+        raise ValueError("x1 must be (m, k) or stacked (nsim, m, k)")
+    _want(x1, "x1", dtypes=(torch.float16, torch.bfloat16, torch.int8))
+    _want(x2, "x2", dtype=x1.dtype)
     nsim = 1 if x1.dim() == 2 else x1.shape[0]
     m, k = x1.shape[-2], x1.shape[-1]
     n = x2.shape[-2] if x2_trans else x2.shape[-1]
@@ -89,12 +112,17 @@ def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_s
         raise ValueError("x1 and x2 must be stacked alike")
     if (x2.shape[-1] if x2_trans else x2.shape[-2]) != k:
         raise ValueError("k mismatch between x1 and x2")
+    quant = x1.dtype == torch.int8
+    _want(bias, "bias", shape=(n,), dtype=torch.bfloat16 if quant else x1.dtype)
+    _want(x1_scale, "x1_scale", dtype=torch.float32, numel=m)
+    _want(x2_scale, "x2_scale", dtype=torch.float32, numel=n)
     if out_dtype is None:
-        out_dtype = torch.bfloat16 if x1.dtype == torch.int8 else x1.dtype
+        out_dtype = torch.bfloat16 if quant else x1.dtype
+    _want(out, "out", shape=(m, n), dtype=out_dtype)
+    dev = _dev(x1, x2, bias, x1_scale, x2_scale, out, flag_counters)
+    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
-    elif out.shape != (m, n) or out.dtype != out_dtype:
-        raise ValueError("out must be (m, n) of out_dtype")
     st = _lib.load().mc2_mm_rs_local(
         x1.data_ptr(), x2.data_ptr(), m, k, n, world_size, rank, nsim, int(bool(x2_trans)),
         _CODES[x1.dtype], _ptr(bias), _ptr(x1_scale), _ptr(x2_scale), _CODES[out_dtype],
@@ -103,15 +131,29 @@ def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_s
     return out
 
 
-def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=None, out=None,
-                    ready_flags=None, flag_counters=None, epoch=0, comm_turn=0):
-    """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out."""
-    dev = _dev(x_gathered, x2, bias, out, flag_counters)
-    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
+def _check_ag(x_gathered, x2, world_size, x2_trans, bias, out):
+    """Shapes of an AllGatherMatmul call: returns (W * m_c, k, n)."""
+    if x_gathered.dim() != 2 or x2.dim() != 2:
+        raise ValueError("x_gathered and x2 must be matrices")
+    _want(x_gathered, "x_gathered", dtypes=_FLOAT16)
+    _want(x2, "x2", dtype=x_gathered.dtype)
     M, k = x_gathered.shape
     if M % world_size:
         raise ValueError("rows of x_gathered must be world_size * m_c")
     n = x2.shape[0] if x2_trans else x2.shape[1]
+    if (x2.shape[1] if x2_trans else x2.shape[0]) != k:
+        raise ValueError("k mismatch between x_gathered and x2")
+    _want(bias, "bias", shape=(n,), dtype=x_gathered.dtype)
+    _want(out, "out", shape=(M, n), dtype=x_gathered.dtype)
+    return M, k, n
+
+
+def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=None, out=None,
+                    ready_flags=None, flag_counters=None, epoch=0, comm_turn=0):
+    """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out."""
+    M, k, n = _check_ag(x_gathered, x2, world_size, x2_trans, bias, out)
+    dev = _dev(x_gathered, x2, bias, out, flag_counters)
+    _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     if out is None:
         out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
     st = _lib.load().mc2_ag_mm_local(
@@ -129,6 +171,8 @@ def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch
     """mc2_ag_mm_local whose tiles wait until in_flags[g] == in_epoch before
     reading segment g of a gathered chunk other than the own one. in_flags:
     world_size * max(comm_turn, 1) int32 on the GPU or in host-pinned memory."""
+    M, k, n = _check_ag(x_gathered, x2, world_size, x2_trans, bias, out)
+    _want(dev_err, "dev_err", **_ERR)
     segs = world_size * max(int(comm_turn), 1)
     if in_flags.dtype not in (torch.int32, torch.uint32) or in_flags.numel() != segs:
         raise ValueError(f"in_flags must hold {segs} int32")
@@ -136,10 +180,6 @@ def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch
     if not in_flags.is_cuda and not in_flags.is_pinned():
         raise ValueError("in_flags must be GPU or host-pinned memory")
     dev = _dev(x_gathered, x2, bias, out, flag_counters, dev_err)
-    M, k = x_gathered.shape
-    if M % world_size:
-        raise ValueError("rows of x_gathered must be world_size * m_c")
-    n = x2.shape[0] if x2_trans else x2.shape[1]
     if out is None:
         out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
     st = _lib.load().mc2_ag_mm_local_inflags(
@@ -162,13 +202,18 @@ def mc2_mm_ar_local(x1, x2, world_size, *, rounding=MC2_AR_ONE_ROUNDING, x2_tran
     partials x1 (W, m, k) @ x2 (W, k, n) (or (W, n, k) with x2_trans), combined
     under `rounding`. A workspace is allocated when the mode needs one and
     none is given."""
-    dev = _dev(x1, x2, bias, out, workspace)
     if x1.dim() != 3 or x2.dim() != 3 or x1.shape[0] != world_size or x2.shape[0] != world_size:
         raise ValueError("x1 and x2 must be stacked (world_size, ., .)")
+    _want(x1, "x1", dtypes=_FLOAT16)
+    _want(x2, "x2", dtype=x1.dtype)
     _, m, k = x1.shape
     n = x2.shape[1] if x2_trans else x2.shape[2]
     if (x2.shape[2] if x2_trans else x2.shape[1]) != k:
         raise ValueError("k mismatch between x1 and x2")
+    _want(bias, "bias", shape=(n,), dtype=x1.dtype)
+    _want(out, "out", shape=(m, n), dtype=x1.dtype)
+    _want(workspace, "workspace", dtype=torch.uint8)
+    dev = _dev(x1, x2, bias, out, workspace)
     if out is None:
         out = torch.empty((m, n), dtype=x1.dtype, device=dev)
     need = mc2_mm_ar_workspace_size(m, n, world_size, x1.dtype, rounding)
@@ -184,6 +229,8 @@ def mc2_mm_ar_local(x1, x2, world_size, *, rounding=MC2_AR_ONE_ROUNDING, x2_tran
 
 def mc2_ar_sum_local(partials, rounding, *, out=None):
     """The all-reduce combining step: partials (W, ...) -> out (...)."""
+    _want(partials, "partials", dtypes=_FLOAT16)
+    _want(out, "out", shape=partials.shape[1:], dtype=partials.dtype)
     dev = _dev(partials, out)
     W = partials.shape[0]
     if out is None:
@@ -195,9 +242,10 @@ def mc2_ar_sum_local(partials, rounding, *, out=None):
 
 
 def mc2_moe_histc(sel, num_experts, *, counts=None, dev_err=None):
+    _want(sel, "sel", dtype=torch.int32)
+    _want(counts, "counts", dtype=torch.int32, numel=num_experts)
+    _want(dev_err, "dev_err", **_ERR)
     dev = _dev(sel, counts, dev_err)
-    if sel.dtype != torch.int32:
-        raise ValueError("sel must be int32")
     if counts is None:
         counts = torch.empty(num_experts, dtype=torch.int32, device=dev)
     st = _lib.load().mc2_moe_histc(sel.data_ptr(), sel.numel(), num_experts, counts.data_ptr(),
@@ -210,16 +258,31 @@ def mc2_moe_permute_workspace_size(T, K, num_experts) -> int:
     return int(_lib.load().mc2_moe_permute_workspace_size(T, K, num_experts))
 
 
-def mc2_moe_permute(x, sel, num_experts, *, permuted=None, sorted_idx=None, unpermute_idx=None,
-                    expert_offsets=None, workspace=None, dev_err=None):
-    """Returns (permuted, sorted_idx, unpermute_idx, expert_offsets)."""
-    dev = _dev(x, sel, permuted, sorted_idx, unpermute_idx, expert_offsets, workspace, dev_err)
+def _check_permute(x, sel, num_experts, permuted, sorted_idx, unpermute_idx, expert_offsets,
+                   dev_err):
+    if x.dim() != 2 or sel.dim() != 2:
+        raise ValueError("x must be (T, H) and sel (T, K)")
     T, H = x.shape
     K = sel.shape[1]
     if sel.dtype != torch.int32 or sel.shape[0] != T:
         raise ValueError("sel must be int32 (T, K)")
     if x.element_size() != 2:
         raise ValueError("x must hold 16-bit elements")
+    _want(permuted, "permuted", shape=(T * K, H), dtype=x.dtype)
+    _want(sorted_idx, "sorted_idx", dtype=torch.int32, numel=T * K)
+    _want(unpermute_idx, "unpermute_idx", dtype=torch.int32, numel=T * K)
+    _want(expert_offsets, "expert_offsets", dtype=torch.int32, numel=num_experts + 1)
+    _want(dev_err, "dev_err", **_ERR)
+    return T, H, K
+
+
+def mc2_moe_permute(x, sel, num_experts, *, permuted=None, sorted_idx=None, unpermute_idx=None,
+                    expert_offsets=None, workspace=None, dev_err=None):
+    """Returns (permuted, sorted_idx, unpermute_idx, expert_offsets)."""
+    T, H, K = _check_permute(x, sel, num_experts, permuted, sorted_idx, unpermute_idx,
+                             expert_offsets, dev_err)
+    _want(workspace, "workspace", dtype=torch.uint8)
+    dev = _dev(x, sel, permuted, sorted_idx, unpermute_idx, expert_offsets, workspace, dev_err)
     if permuted is None:
         permuted = torch.empty((T * K, H), dtype=x.dtype, device=dev)
     if sorted_idx is None:
@@ -240,14 +303,27 @@ def mc2_moe_permute(x, sel, num_experts, *, permuted=None, sorted_idx=None, unpe
     return permuted, sorted_idx, unpermute_idx, expert_offsets
 
 
+def _check_counts(send_counts, recv_counts, num_experts, world_size_src, local_experts):
+    _want(send_counts, "send_counts", dtype=torch.int32, numel=num_experts)
+    _want(recv_counts, "recv_counts", dtype=torch.int32, numel=world_size_src * local_experts)
+
+
 def mc2_gmm_dispatch(send_buf, send_counts, recv_counts, w1, *, ep_rank, num_experts,
                      world_size_src=1, act=MC2_ACT_SWIGLU, h_out=None, dev_err=None):
     """Grouped fc1 (+ SwiGLU) over the rows of the local experts. h_out must
     hold at least as many rows as the local experts receive; by default it has
     as many rows as send_buf."""
-    dev = _dev(send_buf, send_counts, recv_counts, w1, h_out, dev_err)
+    if w1.dim() != 3 or send_buf.dim() != 2:
+        raise ValueError("w1 must be (E_l, H, I2) and send_buf (rows, H)")
     E_l, H, I2 = w1.shape
     n_out = I2 // 2 if act == MC2_ACT_SWIGLU else I2
+    _check_counts(send_counts, recv_counts, num_experts, world_size_src, E_l)
+    _want(w1, "w1", dtype=torch.bfloat16)
+    _want(send_buf, "send_buf", shape=(send_buf.shape[0], H), dtype=torch.bfloat16)
+    if h_out is not None:
+        _want(h_out, "h_out", shape=(h_out.shape[0], n_out), dtype=torch.bfloat16)
+    _want(dev_err, "dev_err", **_ERR)
+    dev = _dev(send_buf, send_counts, recv_counts, w1, h_out, dev_err)
     if h_out is None:
         h_out = torch.empty((send_buf.shape[0], n_out), dtype=torch.bfloat16, device=dev)
     st = _lib.load().mc2_gmm_dispatch(
@@ -261,8 +337,15 @@ def mc2_gmm_dispatch(send_buf, send_counts, recv_counts, w1, *, ep_rank, num_exp
 def mc2_gmm_combine(h, recv_counts, send_counts, w2, combine_buf, *, ep_rank, num_experts,
                     world_size_src=1, dev_err=None):
     """Grouped fc2 written back over the local experts' rows of combine_buf."""
-    dev = _dev(h, recv_counts, send_counts, w2, combine_buf, dev_err)
+    if w2.dim() != 3 or h.dim() != 2 or combine_buf.dim() != 2:
+        raise ValueError("w2 must be (E_l, I, H), h (rows, I) and combine_buf (rows, H)")
     E_l, I, H = w2.shape
+    _check_counts(send_counts, recv_counts, num_experts, world_size_src, E_l)
+    _want(w2, "w2", dtype=torch.bfloat16)
+    _want(h, "h", shape=(h.shape[0], I), dtype=torch.bfloat16)
+    _want(combine_buf, "combine_buf", shape=(combine_buf.shape[0], H), dtype=torch.bfloat16)
+    _want(dev_err, "dev_err", **_ERR)
+    dev = _dev(h, recv_counts, send_counts, w2, combine_buf, dev_err)
     st = _lib.load().mc2_gmm_combine(
         h.data_ptr(), h.shape[0], recv_counts.data_ptr(), send_counts.data_ptr(), world_size_src,
         ep_rank, num_experts, E_l, w2.data_ptr(), I, H, combine_buf.data_ptr(),
@@ -287,11 +370,22 @@ def mc2_gmm_combine_backward(dy_buf, recv_counts, send_counts, w2, h, *, ep_rank
     """Backward of the grouped fc2: returns (dgrad, dW2). dgrad is the fc2
     input gradient (rows of h, I), or with act=MC2_ACT_SWIGLU the gradient of
     the saved fc1 pre-activation g_saved (rows, 2I); dW2 (E_l, I, H) fp32."""
+    if w2.dim() != 3 or h.dim() != 2 or dy_buf.dim() != 2:
+        raise ValueError("w2 must be (E_l, I, H), h (rows, I) and dy_buf (rows, H)")
+    E_l, I, H = w2.shape
+    cols = 2 * I if act == MC2_ACT_SWIGLU else I
+    _check_counts(send_counts, recv_counts, num_experts, world_size_src, E_l)
+    _want(w2, "w2", dtype=torch.bfloat16)
+    _want(dy_buf, "dy_buf", shape=(dy_buf.shape[0], H), dtype=torch.bfloat16)
+    _want(h, "h", shape=(h.shape[0], I), dtype=torch.bfloat16)
+    _want(g_saved, "g_saved", shape=(h.shape[0], 2 * I), dtype=torch.bfloat16)
+    _want(dgrad_out, "dgrad_out", shape=(h.shape[0], cols), dtype=torch.bfloat16)
+    _want(dw2_out, "dw2_out", shape=(E_l, I, H), dtype=torch.float32)
+    _want(workspace, "workspace", dtype=torch.uint8)
+    _want(dev_err, "dev_err", **_ERR)
     dev = _dev(dy_buf, recv_counts, send_counts, w2, h, g_saved, dgrad_out, dw2_out, workspace,
                dev_err)
-    E_l, I, H = w2.shape
     if dgrad_out is None:
-        cols = 2 * I if act == MC2_ACT_SWIGLU else I
         dgrad_out = torch.empty((h.shape[0], cols), dtype=torch.bfloat16, device=dev)
     if dw2_out is None:
         dw2_out = torch.empty((E_l, I, H), dtype=torch.float32, device=dev)
@@ -312,8 +406,18 @@ def mc2_gmm_dispatch_backward(dg, recv_counts, send_counts, w1, send_buf, dx_buf
     """Backward of the grouped fc1: the input gradient goes into the local
     experts' rows of dx_buf (send-buffer layout); returns (dx_buf, dW1) with
     dW1 (E_l, H, I2) fp32."""
-    dev = _dev(dg, recv_counts, send_counts, w1, send_buf, dx_buf, dw1_out, workspace, dev_err)
+    if w1.dim() != 3 or dg.dim() != 2 or send_buf.dim() != 2 or dx_buf.dim() != 2:
+        raise ValueError("w1 must be (E_l, H, I2); dg, send_buf and dx_buf matrices")
     E_l, H, I2 = w1.shape
+    _check_counts(send_counts, recv_counts, num_experts, world_size_src, E_l)
+    _want(w1, "w1", dtype=torch.bfloat16)
+    _want(dg, "dg", shape=(dg.shape[0], I2), dtype=torch.bfloat16)
+    _want(send_buf, "send_buf", shape=(send_buf.shape[0], H), dtype=torch.bfloat16)
+    _want(dx_buf, "dx_buf", shape=(dx_buf.shape[0], H), dtype=torch.bfloat16)
+    _want(dw1_out, "dw1_out", shape=(E_l, H, I2), dtype=torch.float32)
+    _want(workspace, "workspace", dtype=torch.uint8)
+    _want(dev_err, "dev_err", **_ERR)
+    dev = _dev(dg, recv_counts, send_counts, w1, send_buf, dx_buf, dw1_out, workspace, dev_err)
     if dw1_out is None:
         dw1_out = torch.empty((E_l, H, I2), dtype=torch.float32, device=dev)
     need = mc2_gmm_backward_workspace_size(send_buf.shape[0], E_l, H, I2)
@@ -328,9 +432,16 @@ def mc2_gmm_dispatch_backward(dg, recv_counts, send_counts, w1, send_buf, dx_buf
 
 
 def mc2_moe_unpermute(y_full, unpermute_idx, probs, *, out=None, dev_err=None):
-    dev = _dev(y_full, unpermute_idx, probs, out, dev_err)
+    if probs.dim() != 2 or y_full.dim() != 2:
+        raise ValueError("probs must be (T, K) and y_full (rows, H)")
     T, K = probs.shape
     H = y_full.shape[1]
+    _want(y_full, "y_full", dtype=torch.bfloat16)
+    _want(probs, "probs", dtype=torch.float32)
+    _want(unpermute_idx, "unpermute_idx", dtype=torch.int32, numel=T * K)
+    _want(out, "out", shape=(T, H), dtype=torch.bfloat16)
+    _want(dev_err, "dev_err", **_ERR)
+    dev = _dev(y_full, unpermute_idx, probs, out, dev_err)
     if out is None:
         out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     st = _lib.load().mc2_moe_unpermute(

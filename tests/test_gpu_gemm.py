@@ -329,69 +329,3 @@ def test_ag_mm_inflags_timeout_reported_and_state_kept():
     torch.cuda.synchronize()
     assert err.item() == 0 and flags.cpu().tolist() == [2] * W
     assert_tol(to_f64(out), og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16"), "after")
-
-
-# ------------------------------------------------------------------ full sizes
-
-def _sample(m, W, n, rng, per_chunk=6, ncols=48):
-    rows = np.concatenate([c * (m // W) + rng.choice(m // W, per_chunk, replace=False)
-                           for c in range(W)])
-    cols = np.sort(rng.choice(n, ncols, replace=False))
-    return rows, cols
-
-
-@pytest.mark.parametrize("layout", ["kn", "nk"])
-def test_c2_full_ag_mm_sampled(layout):
-    """Config 2 at full size, in the launch configuration the benchmark times:
-    x2 given (k, n), and given as an (n, k) weight passed transposed (the
-    headline)."""
-    d = wl.c2_inputs()
-    if layout == "nk":
-        d = wl.x2_as_nk(d)
-    W = 8
-    flags = torch.zeros(W, dtype=torch.int32, device="cuda")
-    counters = torch.zeros(W, dtype=torch.int32, device="cuda")
-    out = mc2.mc2_ag_mm_local(to_dev(d["x1"], "bf16"), to_dev(d["x2"], "bf16"), W, 0,
-                              x2_trans=d["x2_trans"], ready_flags=flags, flag_counters=counters,
-                              epoch=1)
-    torch.cuda.synchronize()
-    assert flags.cpu().tolist() == [1] * W
-    rows, cols = _sample(8192, W, 3072, np.random.default_rng(0))
-    ref = og.ag_mm(d["x1"], d["x2"], world_size=W, in_dtype="bf16", x2_trans=d["x2_trans"],
-                   rows=rows, cols=cols)
-    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, f"C2 {layout}")
-    assert torch.isfinite(out.float()).all()
-
-
-@pytest.mark.parametrize("layout", ["kn", "nk"])
-def test_c3_full_int8_sampled(layout):
-    d = wl.c3_inputs()
-    if layout == "nk":
-        d = wl.x2_as_nk(d)
-    out = _run_rs(d, 4, 0)
-    rows, cols = _sample(4096, 4, 2048, np.random.default_rng(1))
-    ref = _oracle_rs(d, 4, rows=rows, cols=cols)
-    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, f"C3 bf16 {layout}")
-    raw = _run_rs(d, 4, 0, out_dtype="i32")
-    np.testing.assert_array_equal(to_f64(raw)[np.ix_(rows, cols)],
-                                  _oracle_rs(d, 4, out_dtype="i32", rows=rows, cols=cols))
-
-
-@pytest.mark.parametrize("layout", ["kn", "nk"])
-def test_c5_full_sampled(layout):
-    a, b = wl.c5_inputs()
-    if layout == "nk":
-        a, b = wl.x2_as_nk(a), wl.x2_as_nk(b)
-    W = 8
-    out = mc2.mc2_ag_mm_local(to_dev(a["x1"], "bf16"), to_dev(a["x2"], "bf16"), W, 0,
-                              x2_trans=a["x2_trans"])
-    torch.cuda.synchronize()
-    rows, cols = _sample(16384, W, 3584, np.random.default_rng(2), per_chunk=4)
-    ref = og.ag_mm(a["x1"], a["x2"], world_size=W, in_dtype="bf16", x2_trans=a["x2_trans"],
-                   rows=rows, cols=cols)
-    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, f"C5a {layout}")
-    del out
-    out = _run_rs(b, W, 0)
-    rows, cols = _sample(16384, W, 8192, np.random.default_rng(3), per_chunk=4)
-    ref = _oracle_rs(b, W, rows=rows, cols=cols)
-    assert_tol(to_f64(out)[np.ix_(rows, cols)], ref, f"C5b {layout}")

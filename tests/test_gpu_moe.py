@@ -203,34 +203,3 @@ def test_moe_chain_small(standins):
     assert_tol(to_f64(g["h"])[:nloc], r["h"], "fc1+swiglu")
     assert_tol(to_f64(g["buf"]), r["y_full"], "fc2 combine buffer")
     assert_tol(to_f64(g["out"]), r["out"], "unpermute out")
-
-
-def test_c4_full_sampled():
-    """Config 4 at full size: counts and indices bit-exact everywhere; the
-    permuted rows bit-exact; GMM and unpermute outputs on sampled rows."""
-    d = wl.c4_inputs()
-    g = _gpu_chain(d)
-    counts = om.histc(d["sel"], 128)
-    np.testing.assert_array_equal(g["counts"].cpu().numpy(), counts)
-    p = om.permute(np.zeros((d["T"], 1), np.uint16), d["sel"], 128)
-    np.testing.assert_array_equal(g["sidx"].cpu().numpy(), p["sorted_idx"])
-    np.testing.assert_array_equal(g["uidx"].cpu().numpy(), p["unpermute_idx"])
-    sidx = p["sorted_idx"]
-    rng = np.random.default_rng(5)
-    pos = rng.choice(d["T"] * d["K"], 512, replace=False)
-    got_rows = g["perm"][torch.from_numpy(pos).cuda()].view(torch.int16).cpu().numpy().view(np.uint16)
-    np.testing.assert_array_equal(got_rows, d["x"][sidx[pos] // d["K"]])
-    # fc1 + SwiGLU and fc2 on sampled local rows, from the oracle's own rows
-    nloc = int(counts[:16].sum())
-    rows = np.sort(rng.choice(nloc, 256, replace=False))
-    slots = sidx[rows]
-    h_ref, y_ref = om.expert_ffn_rows(d["x"][slots // d["K"]], d["sel"].reshape(-1)[slots],
-                                      d["w1"], d["w2"])
-    assert_tol(to_f64(g["h"])[rows], h_ref, "C4 fc1+swiglu")
-    assert_tol(to_f64(g["buf"])[rows], y_ref, "C4 fc2")
-    assert bool((g["buf"][nloc:] == 0).all())
-    # unpermuted outputs of sampled tokens
-    toks = np.sort(rng.choice(d["T"], 128, replace=False))
-    ref = om.token_outputs(d["x"], d["sel"], d["probs"], d["w1"], d["w2"], toks, ep_rank=0,
-                           local_experts=16)
-    assert_tol(to_f64(g["out"])[toks], ref, "C4 unpermute")

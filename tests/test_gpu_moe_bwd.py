@@ -240,9 +240,40 @@ def test_weight_gradient_many_transpose_items_ragged_columns():
     _, ref_dw2 = om.combine_backward(b["dy"], recv, send_counts, ep_rank=0, local_experts=5,
                                      w2=d["w2"], h=b["h"], act="none")
     _assert_wgrad(dw2.cpu().numpy(), ref_dw2, _dec(b["h"]), _dec(b["dy"]), recv, "many-item dW2")
-    _, ref_dw1 = om.dispatch_backward(b["dg"], recv, send_counts, ep_rank=0, local_experts=5,
-                                      w1=d["w1"], send_buf=b["send"], dx_buf=np.zeros((n, H)))
+    ref_dx, ref_dw1 = om.dispatch_backward(b["dg"], recv, send_counts, ep_rank=0,
+                                           local_experts=5, w1=d["w1"], send_buf=b["send"],
+                                           dx_buf=np.zeros((n, H)))
     _assert_wgrad(dw1.cpu().numpy(), ref_dw1, _dec(b["send"]), _dec(b["dg"]), recv, "many-item dW1")
+    # the input gradient too, every row: its 159 row tiles by 2 column tiles
+    # leave a last round of 62 tiles on 256 CUs, run as 128-row halves
+    assert_tol(to_f64(dx), ref_dx, "many-item dX")
+
+
+def test_swiglu_combine_backward_half_tile_last_round():
+    """The fused SwiGLU backward in the last dispatch round of the grouped
+    kernel: groups of 5000, 300, 3 and 10900 rows give 66 row tiles by 4
+    column tiles (I = 1024), 264 tiles on 256 CUs, so the last 8 run as
+    128-row halves; they are the last row tiles of the 10900-row group, whose
+    final tile holds 148 rows (its upper half is not empty). H = 200 puts a
+    tail in K. Every element of dG against the oracle."""
+    H, I = 200, 1024
+    send_counts = np.array([5000, 300, 3, 10900], dtype=np.int32)
+    recv = send_counts.copy()
+    n = int(recv.sum())
+    d = wl.moe_inputs(seed=78, tokens=16, hidden=H, num_experts=4, topk=1, local_experts=4,
+                      inter=I, w_std=0.05)
+    b = wl.moe_backward_inputs(79, n, H, I)
+    dgrad = torch.full((n, 2 * I), 7.0, dtype=torch.bfloat16, device="cuda")
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    mc2.mc2_gmm_combine_backward(to_dev(b["dy"], "bf16"), to_dev(recv), to_dev(send_counts),
+                                 to_dev(d["w2"], "bf16"), to_dev(b["h"], "bf16"), ep_rank=0,
+                                 num_experts=4, act=mc2.MC2_ACT_SWIGLU,
+                                 g_saved=to_dev(b["g"], "bf16"), dgrad_out=dgrad, dev_err=err)
+    torch.cuda.synchronize()
+    assert err.item() == 0
+    ref, _ = om.combine_backward(b["dy"], recv, send_counts, ep_rank=0, local_experts=4,
+                                 w2=d["w2"], h=b["h"], g_saved=b["g"], act="swiglu")
+    assert_tol(to_f64(dgrad), ref, "SwiGLU dG with a half-tile last round")
 
 
 def test_backward_no_local_rows():
