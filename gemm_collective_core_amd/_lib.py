@@ -25,6 +25,7 @@ SIGNATURES = {
     "mc2_moe_histc": (_I, [_P, _I64, _I, _P, _P, _P]),
     "mc2_moe_permute_workspace_size": (C.c_size_t, [_I64, _I, _I]),
     "mc2_moe_permute": (_I, [_P, _I64, _I64, _P, _I, _I, _P, _P, _P, _P, _P, C.c_size_t, _P, _P]),
+    "mc2_moe_permute_noalloc": (_I, [_P, _I64, _I64, _P, _I, _I, _P, _P, _P, _P, _P, _P]),
     "mc2_gmm_dispatch": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _I, _P, _I64, _P,
                               _P]),
     "mc2_gmm_combine": (_I, [_P, _I64, _P, _P, _I, _I, _I, _I, _P, _I64, _I64, _P, _I64, _P, _P]),

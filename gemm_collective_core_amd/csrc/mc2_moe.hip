@@ -5,6 +5,8 @@
 //
 // These kernels move bytes, not FLOPs: they are written for coalesced 16-byte
 // accesses and for reading each token row once.
+#include <mutex>
+
 #include "../../include/mc2.h"
 #include "mc2_common.hpp"
 #include "mc2_host.hpp"
@@ -361,6 +363,53 @@ extern "C" int mc2_moe_permute(const void* x, int64_t T, int64_t H, const int32_
                      ws_total, static_cast<uint16_t*>(permuted), sorted_idx, unpermute_idx,
                      expert_offsets);
   return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
+}
+
+// ------------------------------------------------- permute without allocation
+//
+// The counting workspace of the permute (per-block expert counts and expert
+// totals) in a file-scope device array, for callers that cannot allocate.
+// Each device holds its own copy; its address is looked up once per device
+// with hipGetSymbolAddress (the array's name in host code is only a stand-in)
+// and every launch gets that address. The count and scan kernels overwrite
+// every entry the scatter reads, so nothing needs clearing between calls.
+
+constexpr size_t kScratchBytes = MC2_PERMUTE_SCRATCH_BYTES;
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's scratch array, or NULL on a runtime error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" int mc2_moe_permute_noalloc(const void* x, int64_t T, int64_t H, const int32_t* sel,
+                                       int K, int num_experts, void* permuted,
+                                       int32_t* sorted_idx, int32_t* unpermute_idx,
+                                       int32_t* expert_offsets, int32_t* dev_err,
+                                       hipStream_t stream) {
+  if (!x || !sel || !permuted || !sorted_idx || !unpermute_idx || !expert_offsets)
+    return MC2_ERR_NULL;
+  if (T < 1 || K < 1 || K > 64 || num_experts < 1 || num_experts > kMaxExperts) return MC2_ERR_SHAPE;
+  const size_t need = mc2_moe_permute_workspace_size(T, K, num_experts);
+  if (need == 0 || need > kScratchBytes) return MC2_ERR_WORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return MC2_ERR_HIP;
+  return mc2_moe_permute(x, T, H, sel, K, num_experts, permuted, sorted_idx, unpermute_idx,
+                         expert_offsets, ws, kScratchBytes, dev_err, stream);
 }
 
 extern "C" int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermute_idx,

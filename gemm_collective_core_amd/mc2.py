@@ -303,6 +303,27 @@ def mc2_moe_permute(x, sel, num_experts, *, permuted=None, sorted_idx=None, unpe
     return permuted, sorted_idx, unpermute_idx, expert_offsets
 
 
+MC2_PERMUTE_SCRATCH_BYTES = 4 << 20
+
+
+def mc2_moe_permute_noalloc(x, sel, num_experts, *, permuted, sorted_idx, unpermute_idx,
+                            expert_offsets, dev_err=None):
+    """mc2_moe_permute with the library's own per-device counting workspace:
+    the C call allocates nothing, so every output must be passed in. Calls
+    that overlap on one device share that workspace and must be ordered."""
+    if any(t is None for t in (permuted, sorted_idx, unpermute_idx, expert_offsets)):
+        raise ValueError("every output must be passed in")
+    T, H, K = _check_permute(x, sel, num_experts, permuted, sorted_idx, unpermute_idx,
+                             expert_offsets, dev_err)
+    dev = _dev(x, sel, permuted, sorted_idx, unpermute_idx, expert_offsets, dev_err)
+    st = _lib.load().mc2_moe_permute_noalloc(
+        x.data_ptr(), T, H, sel.data_ptr(), K, num_experts, permuted.data_ptr(),
+        sorted_idx.data_ptr(), unpermute_idx.data_ptr(), expert_offsets.data_ptr(),
+        _ptr(dev_err), _stream(dev))
+    _check("mc2_moe_permute_noalloc", st)
+    return permuted, sorted_idx, unpermute_idx, expert_offsets
+
+
 def _check_counts(send_counts, recv_counts, num_experts, world_size_src, local_experts):
     _want(send_counts, "send_counts", dtype=torch.int32, numel=num_experts)
     _want(recv_counts, "recv_counts", dtype=torch.int32, numel=world_size_src * local_experts)

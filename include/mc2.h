@@ -257,6 +257,27 @@ int mc2_moe_permute(const void* x, int64_t T, int64_t H, const int32_t* sel, int
                     size_t ws_bytes, int32_t* dev_err, hipStream_t stream);
 
 /*
+ * mc2_moe_permute_noalloc -- mc2_moe_permute for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation). Same arguments, results and errors as
+ * mc2_moe_permute, without the workspace: the counting workspace is a
+ * library-owned device array of MC2_PERMUTE_SCRATCH_BYTES bytes per device
+ * (held until the process ends). The call itself allocates nothing.
+ * Returns MC2_ERR_WORKSPACE when mc2_moe_permute_workspace_size(T, K, E)
+ * exceeds MC2_PERMUTE_SCRATCH_BYTES, i.e. when E * ceil(T / floor(256 / K))
+ * + E exceeds 1048576 four-byte entries (131072 tokens at K = 8 and E = 128
+ * fit; the MoE workload's 32768 tokens use an eighth). Every call on one
+ * device shares that device's array: calls that overlap on one device
+ * (concurrent streams) race and must be ordered by the caller.
+ */
+#define MC2_PERMUTE_SCRATCH_BYTES ((size_t)4 << 20)
+
+int mc2_moe_permute_noalloc(const void* x, int64_t T, int64_t H, const int32_t* sel, int K,
+                            int num_experts, void* permuted, int32_t* sorted_idx,
+                            int32_t* unpermute_idx, int32_t* expert_offsets, int32_t* dev_err,
+                            hipStream_t stream);
+
+/*
  * mc2_gmm_dispatch -- GroupedMatmul part of the dispatch segment
  * [EP "执行路径": AllToAllv -> GroupedMatmul(fc1), then swiglu].
  *

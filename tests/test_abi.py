@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -122,6 +122,18 @@ def test_moe_entry_points_reject(lib):
     assert U(FAKE, 10, FAKE, FAKE, 4, 0, 64, FAKE, None, None) == ERR_SHAPE
     assert U(FAKE, 10, FAKE, FAKE, 4, 2, 4, FAKE, None, None) == ERR_SHAPE
     assert U(FAKE, 10, FAKE, FAKE, 4, 2, 68, FAKE, None, None) == ERR_ALIGN
+
+
+def test_noalloc_permute_rejects_sizes_beyond_its_scratch(lib):
+    """The allocation-free permute checks the size against its fixed scratch
+    array before looking the array up or launching anything."""
+    T, K, E = 1 << 20, 8, 128
+    assert lib.mc2_moe_permute_workspace_size(T, K, E) > (4 << 20)
+    assert lib.mc2_moe_permute_workspace_size(131072, 8, 128) <= (4 << 20)
+    P = lib.mc2_moe_permute_noalloc
+    assert P(FAKE, T, 64, FAKE, K, E, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_WS
+    assert P(FAKE, 100, 64, FAKE, 65, 16, FAKE, FAKE, FAKE, FAKE, None, None) == ERR_SHAPE
+    assert P(FAKE, 100, 64, FAKE, 8, 16, FAKE, None, FAKE, FAKE, None, None) == ERR_NULL
 
 
 def test_ag_mm_inflags_validates(lib):

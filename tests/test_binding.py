@@ -102,6 +102,18 @@ def test_moe_histc_permute_unpermute_checks():
     _raises(lambda: mc2.mc2_moe_unpermute(z(T * K, H, dtype=f16), idx, probs), "y_full must be")
 
 
+def test_moe_noalloc_permute_checks():
+    T, K, E, H = 10, 4, 16, 64
+    x, sel = z(T, H), z(T, K, dtype=i32)
+    outs = dict(permuted=z(T * K, H), sorted_idx=z(T * K, dtype=i32),
+                unpermute_idx=z(T * K, dtype=i32), expert_offsets=z(E + 1, dtype=i32))
+    _raises(lambda: mc2.mc2_moe_permute_noalloc(x, sel, E, **outs), ON_GPU)
+    bad = dict(outs, expert_offsets=z(E, dtype=i32))
+    _raises(lambda: mc2.mc2_moe_permute_noalloc(x, sel, E, **bad), "expert_offsets must hold")
+    bad = dict(outs, permuted=None)
+    _raises(lambda: mc2.mc2_moe_permute_noalloc(x, sel, E, **bad), "every output")
+
+
 def test_gmm_checks():
     E, El, H, I = 16, 4, 64, 32
     sc, rc = z(E, dtype=i32), z(El, dtype=i32)
