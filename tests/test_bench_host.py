@@ -36,11 +36,22 @@ def test_hash_follows_code(monkeypatch, tmp_path):
 
 
 def test_traffic_record_is_consistent():
-    """The committed record's totals are the scaled counters it lists."""
+    """The committed record's totals are the scaled counters it lists, and
+    the read scale taken from the plain device copy agrees with the one from
+    the one-tile GEMM whose operands pass once through the loads into LDS."""
     with open(os.path.join(bench.ROOT, bench.TRAFFIC_FILE), encoding="utf-8") as f:
         rec = json.load(f)
-    rd = rec["fetch_size_kib_per_dispatch"] * 1024 * rec["fetch_scale"]
-    wr = rec["write_size_kib_per_dispatch"] * 1024 * rec["write_scale"]
+    fetch = rec["fetch_size_kib_per_dispatch"]
+    write = rec["write_size_kib_per_dispatch"]
+    assert abs(fetch["mean"] - (fetch["c5a_ag_mm"] + fetch["c5b_sim_rs"]) / 2) < 1e-6 * fetch["mean"]
+    rd = fetch["mean"] * 1024 * rec["fetch_scale"]
+    wr = write["mean"] * 1024 * rec["write_scale"]
     assert abs(rd - rec["hbm_read_bytes_per_launch"]) < 1e-6 * rd
     assert abs(wr - rec["hbm_write_bytes_per_launch"]) < 1e-6 * wr
     assert abs(rd + wr - rec["traffic_bytes_per_launch"]) < 1e-6 * (rd + wr)
+    lds = rec["calibration_lds_gemm"]
+    assert abs(lds["fetch_scale"] / rec["fetch_scale"] - 1) < 0.01
+    assert rec["launch"] == bench.HEADLINE_LAUNCH
+    # every launch writes its output exactly once
+    out_bytes = 2 * (bench.C5A[0] * bench.C5A[2] + bench.C5B[0] * bench.C5B[2]) / 2
+    assert abs(wr / out_bytes - 1) < 0.01
