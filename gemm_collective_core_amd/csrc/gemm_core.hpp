@@ -68,7 +68,9 @@ typedef MC2_LDS char lds_t;
 template <int BM_, int BN_, int WM_, int WN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
-  static_assert(WM * WN == 8, "eight waves per workgroup");
+  static constexpr int NW = WM * WN;    // waves per workgroup
+  static constexpr int NT = NW * 64;    // threads per workgroup
+  static_assert(NW == 8 || NW == 4, "eight or four waves per workgroup");
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "tile not divisible");
@@ -293,6 +295,7 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
   constexpr int CE = 16 / ES;             // K values per 16-byte chunk
   constexpr int NA = TS::BM / 64;         // A loads per wave per stage
   constexpr int NB = TS::BN / 64;         // B loads per wave per stage
+  static_assert(TS::NW == 8, "the eight-wave schedule");
   static_assert(TS::BN == 256 || (ES == 2 && !BT), "192-column tiles: 16-bit row-major B only");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
@@ -473,6 +476,7 @@ constexpr int kCpolWriteThrough = 0x11;
 // that raise ready flags; every byte offset below 2^31), they write through
 // to memory instead, so the L2 write-back of the flag release that follows
 // has almost nothing to write (measured: about half the cost of the flags).
+template <int NT = kThreads>
 __device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int tile_row_bytes,
                                              int tile_rows, char* out, int64_t ldo, int64_t nrows,
                                              int64_t col_byte0, int64_t row_bytes_valid,
@@ -481,7 +485,7 @@ __device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int t
   const int total = tile_rows * cpr;
   if (write_through) {
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(out);
-    for (int q = threadIdx.x; q < total; q += kThreads) {
+    for (int q = threadIdx.x; q < total; q += NT) {
       const int r = q / cpr, c = q - r * cpr;
       if (r < nrows && col_byte0 + c * 16 < row_bytes_valid)
         __builtin_amdgcn_raw_buffer_store_b128(
@@ -490,7 +494,7 @@ __device__ __forceinline__ void store_staged(const lds_t* smem, int pitch, int t
     }
     return;
   }
-  for (int q = threadIdx.x; q < total; q += kThreads) {
+  for (int q = threadIdx.x; q < total; q += NT) {
     const int r = q / cpr, c = q - r * cpr;
     if (r < nrows && col_byte0 + c * 16 < row_bytes_valid)
       __builtin_nontemporal_store(*reinterpret_cast<const MC2_LDS u32x4_t*>(smem + r * pitch + c * 16),

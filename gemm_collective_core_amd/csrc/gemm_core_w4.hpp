@@ -1,0 +1,309 @@
+// Four-wave main loop of the MFMA contraction for operands held K-contiguous
+// (A as (m, k) and B as (n, k)), gfx950.
+//
+// Workgroup: 4 waves = 256 threads, one wave per SIMD, each wave owning a
+// 128 x 128 (or, for 128-row tiles, 64 x 128) sub-tile of a 256 x 256 output
+// tile: 8 x 8 blocks of 16 x 16, 256 fp32 accumulators per lane, held in the
+// accumulation registers. Against eight waves of 128 x 64 this reads a third
+// less from LDS per MFMA (each wave's A rows serve 128 columns instead of 64),
+// and with one wave per SIMD no wave waits for a faster partner at the stage
+// barrier.
+//
+// K stages, LDS layout, swizzle and the loads straight into LDS are those of
+// the eight-wave loop (gemm_core.hpp): a stage holds 128 bytes of K per row,
+// two stages live in a two-buffer ring, and a load instruction moves 8 rows
+// of 128 bytes.
+//
+// One wave issues everything in one stream, so the stage is a fixed
+// interleave of its 2 x 64 MFMAs (16 cycles each) with the memory
+// instructions, one memory instruction after an MFMA at most, so that a load
+// the memory pipeline is slow to take stalls the wave for at most the MFMA's
+// own latency:
+//   k-step 0, MFMA slots 0..63: the 16 operand reads of k-step 1 after the
+//     first 16 MFMAs; at slot kBar the wave waits for them and for its own
+//     loads of the next stage, and the workgroup barrier follows (every wave
+//     is done with this stage's buffer and every load of the next stage has
+//     landed); then the loads of the stage after next into the buffer just
+//     released, one every second slot;
+//   k-step 1, slots 64..127: the 16 operand reads of the next stage's k-step
+//     0, one every second slot.
+// Every LDS read is inline assembly (the compiler would otherwise wait for
+// all loads before any LDS read); each k-step begins with an lgkmcnt(0) wait
+// for the reads issued during the previous one.
+#pragma once
+
+#include <utility>
+
+#include "gemm_core.hpp"
+
+namespace mc2 {
+
+template <class F, int... Is>
+__device__ __forceinline__ void sfor_impl(F&& f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+// f(integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <int N, class F>
+__device__ __forceinline__ void sfor(F&& f) {
+  sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// 16-byte LDS read at addr + OFF; valid only after a matching lgkm_wait.
+template <int OFF>
+__device__ __forceinline__ u32x4_t lds_rd128_at(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds_read offset field");
+  u32x4_t v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF) : "memory");
+  return v;
+}
+
+// MFMAs as inline assembly with the accumulators in the accumulation
+// registers ("a" operands): 256 accumulators per lane leave the vector
+// registers to the operands. init() starts an accumulator (C = 0), acc()
+// adds to it. The compiler does not see these as MFMAs, so it inserts no
+// wait states for their results: within the loop an accumulator is reused
+// only 64 MFMAs later, and settle() waits before anything else reads them.
+template <Elem E> struct MmaA;
+template <> struct MmaA<Elem::BF16> {
+  static __device__ __forceinline__ void init(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void acc(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct MmaA<Elem::F16> {
+  static __device__ __forceinline__ void init(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void acc(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+template <> struct MmaA<Elem::I8> {
+  static __device__ __forceinline__ void init(i32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, 0" : "=a"(c) : "v"(a), "v"(b));
+  }
+  static __device__ __forceinline__ void acc(i32x4_t& c, u32x4_t a, u32x4_t b) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(c) : "v"(a), "v"(b));
+  }
+};
+
+// Load j of a stage is issued at slot a + 1 + (j * span) / nl; the load
+// issued at slot q, or -1.
+constexpr int load_slot_index(int q, int a, int span, int nl) {
+  for (int j = 0; j < nl; ++j)
+    if (a + 1 + (j * span) / nl == q) return j;
+  return -1;
+}
+
+// KTAIL: the shard's K extent may end inside a stage, so every load checks
+// its lanes against the K values left (lanes past the end load zeros);
+// without it (K a multiple of the stage) the loads carry no per-lane check.
+template <Elem E, class TS, bool KTAIL>
+__device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t lda, int64_t row0,
+                                            int64_t row_last, const BDesc& B, int64_t col0,
+                                            const KSpan& ks,
+                                            typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN]) {
+  constexpr int ES = ElemInfo<E>::bytes;
+  constexpr int KE = kKBytes / ES;  // K values per stage
+  constexpr int CE = 16 / ES;       // K values per 16-byte chunk
+  constexpr int FM = TS::FM, FN = TS::FN;
+  constexpr int NA = TS::BM / 32;   // A loads per wave per stage (8 rows each, 4 waves)
+  constexpr int NB = TS::BN / 32;   // B loads per wave per stage
+  constexpr int NL = NA + NB;
+  constexpr int NR = FM + FN;       // operand reads per wave per k-step
+  static_assert(TS::NW == 4 && TS::BN == 256, "four waves, 256-column tiles");
+  static_assert(NL <= 63, "vmcnt range of the prologue");
+  constexpr int MM = FM * FN;       // MFMA slots per k-step
+  // Slots q = 0 .. 2 MM - 1 of a stage (k-step 1 from MM on), one MFMA each:
+  //   q < NR        the k-step-1 operand reads of this stage;
+  //   kBarA         wait for them, barrier: this stage's buffer is free;
+  //   load slots    the loads of the stage after next into that buffer,
+  //                 spread evenly up to kBarB so that the CU's load path
+  //                 (about one 1 KiB load per 18 cycles) never queues them;
+  //   kBarB         wait for this wave's loads of the next stage, barrier;
+  //   after kBarB   the next stage's k-step-0 operand reads.
+  constexpr int kBarA = NR + 4;
+  constexpr int kBarB = 2 * MM - NR - 8;
+  constexpr int kLSpan = kBarB - kBarA - 1;
+  static_assert(kLSpan >= NL && kBarB + NR < 2 * MM, "slots for the loads and the reads");
+  const int tid = threadIdx.x, lane = tid & 63;
+  // the wave index as a wave-uniform value: the LDS destinations of the loads
+  // (M0) are then scalar arithmetic
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto load_index = [](int q) constexpr { return load_slot_index(q, kBarA, kLSpan, NL); };
+  const int wrow0 = (wave / TS::WN) * TS::WTM;
+  const int wcol0 = (wave % TS::WN) * TS::WTN;
+
+  // Per-lane offsets of this wave's loads: lane -> row (lane >> 3) of the 8
+  // rows a load writes, physical chunk lane & 7, holding logical chunk
+  // (lane & 7) ^ swizzle.
+  uint32_t l_off[NL];
+  int l_key[NL];
+#pragma unroll
+  for (int j = 0; j < NL; ++j) {
+    const bool isa = j < NA;
+    const int r = 8 * ((isa ? NA : NB) * wave + (isa ? j : j - NA)) + (lane >> 3);
+    const int c = (row_off(r, lane & 7) - r * kKBytes) >> 4;
+    if (isa) {
+      int64_t gr = row0 + r;
+      gr = gr < row_last ? gr : row_last;
+      l_off[j] = static_cast<uint32_t>((gr - row0) * lda + c * 16);
+    } else {
+      int64_t gc = col0 + r;
+      gc = gc < B.n - 1 ? gc : B.n - 1;
+      l_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
+    }
+    l_key[j] = c * CE;
+  }
+  const char* a_base = A + row0 * lda;
+  const char* b_base = B.base + col0 * B.ld;
+
+  // Loads of stage it: the buffer resources are formed once per stage; a
+  // stage past the last one gets resources of no records, so its loads (the
+  // loop issues them unconditionally, with no branch in the MFMA stream)
+  // touch no memory and write zeros into a buffer nobody reads any more.
+  struct StageLd {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    int kleft;  // K values left in this shard (clamped)
+    lds_t* st;
+  };
+  // Stages are loaded in order; (lw, lkt) is the shard and K stage of the
+  // next stage to load, advanced with scalar adds (no division per stage).
+  int ld_it = 0, lw = 0, lkt = 0;
+  auto prep = [&]() {
+    StageLd s;
+    const int64_t kdone = static_cast<int64_t>(lkt) * KE;
+    const int64_t kl = ks.k - kdone;
+    s.kleft = static_cast<int>(kl < (1 << 30) ? kl : (1 << 30));
+    s.st = smem + (ld_it & 1) * TS::kStageBytes;
+    const int nrec = ld_it < ks.niters ? 0x7ffffff0 : 0;
+    s.ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(a_base + lw * ks.a_shard + kdone * ES), 0, nrec, kBufFlags);
+    s.rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(b_base + lw * ks.b_shard + kdone * ES), 0, nrec, kBufFlags);
+    ++ld_it;
+    if (++lkt == ks.ktiles) {
+      lkt = 0;
+      ++lw;
+    }
+    return s;
+  };
+  auto issue_j = [&](const StageLd& s, int j) {
+    uint32_t off = l_off[j];
+    if constexpr (KTAIL) off = l_key[j] < s.kleft ? off : kOffNone;
+    if (j < NA)
+      dma16(s.ra, s.st + 8 * (NA * wave + j) * kKBytes, off);
+    else
+      dma16(s.rb, s.st + TS::kABytes + 8 * (NB * wave + (j - NA)) * kKBytes, off);
+  };
+
+  // LDS read addresses of the wave's first fragment (row wrow0 + (lane & 15)
+  // of A, column wcol0 + (lane & 15) of B) for k-step ks of buffer p; the
+  // other fragments sit 16 rows (2048 bytes) further on, an immediate offset.
+  const uint32_t s0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(smem));
+  uint32_t adA[2][2], adB[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int k2 = 0; k2 < 2; ++k2) {
+      const int ch = k2 * 4 + (lane >> 4);
+      adA[p][k2] = s0 + p * TS::kStageBytes + row_off(wrow0 + (lane & 15), ch);
+      adB[p][k2] = s0 + p * TS::kStageBytes + TS::kABytes + row_off(wcol0 + (lane & 15), ch);
+    }
+
+  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
+  // operand read number i of a k-step: B fragments first, then A
+  auto read_op = [&](auto I, uint32_t adA_, uint32_t adB_, u32x4_t (&a)[FM], u32x4_t (&b)[FN]) {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i < FN)
+      b[i] = lds_rd128_at<i * 16 * kKBytes>(adB_);
+    else
+      a[i - FN] = lds_rd128_at<(i - FN) * 16 * kKBytes>(adA_);
+  };
+  auto tie = [&](u32x4_t (&a)[FM], u32x4_t (&b)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a[i]));
+#pragma unroll
+    for (int i = 0; i < FN; ++i) asm volatile("" : "+v"(b[i]));
+  };
+
+  const int n = ks.niters;  // at least 1
+  StageLd nx;
+  {
+    nx = prep();  // stage 0
+#pragma unroll
+    for (int j = 0; j < NL; ++j) issue_j(nx, j);
+    nx = prep();  // stage 1 (no records when there is a single stage)
+#pragma unroll
+    for (int j = 0; j < NL; ++j) issue_j(nx, j);
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");  // stage 0 has landed
+    bar_sync();
+    sfor<NR>([&](auto I) { read_op(I, adA[0][0], adB[0][0], a0, b0); });
+  }
+
+  // One stage from buffer P; the first stage starts the accumulators.
+  auto stage = [&](auto Pc, auto First, int it) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr bool FIRST = decltype(First)::value;
+    lgkm_wait(0);  // this stage's k-step-0 operands (read during the previous stage)
+    tie(a0, b0);
+    sfor<2 * MM>([&](auto Q) {
+      constexpr int q = decltype(Q)::value;
+      constexpr int s = q % MM, fm = s / FN, fn = s % FN;
+      if constexpr (q == MM) tie(a1, b1);
+      if constexpr (q < MM) {
+        if constexpr (FIRST)
+          MmaA<E>::init(acc[fm][fn], a0[fm], b0[fn]);
+        else
+          MmaA<E>::acc(acc[fm][fn], a0[fm], b0[fn]);
+      } else {
+        MmaA<E>::acc(acc[fm][fn], a1[fm], b1[fn]);
+      }
+      if constexpr (q < NR) {
+        read_op(std::integral_constant<int, q>{}, adA[P][1], adB[P][1], a1, b1);
+      } else if constexpr (q == kBarA) {
+        lgkm_wait(0);  // every read of this stage's buffer is done
+        bar_sync();    // ... by every wave: the buffer may be refilled
+        nx = prep();  // stage it + 2
+      } else if constexpr (load_index(q) >= 0) {
+        issue_j(nx, load_index(q));
+      } else if constexpr (q == kBarB) {
+        // this wave's loads of the next stage have landed (the NL loads of
+        // the stage after next, issued since kBarA, may still be in flight)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+        bar_sync();  // ... and every wave's
+      } else if constexpr (q > kBarB && (q - kBarB - 1) < NR) {
+        // the next stage's k-step-0 operands (after the last stage: reads of
+        // a buffer nobody writes any more, never used)
+        read_op(std::integral_constant<int, q - kBarB - 1>{}, adA[1 - P][0], adB[1 - P][0], a0, b0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using T = std::true_type;
+  using F = std::false_type;
+  stage(I0{}, T{}, 0);
+  for (int it = 1; it < n; it += 2) {
+    stage(I1{}, F{}, it);
+    if (it + 1 < n) stage(I0{}, F{}, it + 1);
+  }
+  // the last stage's reads of the next stage's operands (never used) land in
+  // registers that stay allocated until they have (an asm output counts as
+  // written at once, so without this use the compiler could reuse them early)
+  lgkm_wait(0);
+  tie(a0, b0);
+  wait_vmcnt0();
+  bar_sync();
+  // the last MFMAs' results are complete before anything reads them
+  asm volatile("s_nop 15\n\ts_nop 15\n\ts_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
+}
+
+}  // namespace mc2

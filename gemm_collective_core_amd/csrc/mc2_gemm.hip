@@ -75,7 +75,7 @@ constexpr int chunked_smem() {
 // inside a piece row-block fastest, so that a run of consecutive tiles forms a
 // compact block and the segments complete roughly in order. `weight` is the
 // tile's share of the segment counter (2 for a whole tile, 1 for a half).
-template <Elem E, bool BT, class TS, Out O>
+template <Elem E, bool BT, class TS, Out O, bool KT>
 __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, int tile, int half,
                                              uint32_t weight) {
   constexpr int OS = OutInfo<O>::bytes;
@@ -111,7 +111,10 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
   typename Mma<E>::acc_t acc[TS::FM][TS::FN];
   BDesc bd{p.B, p.ldb, p.n};
   PlainCols cm{col0, p.n - 16 / ElemInfo<E>::bytes};
-  mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
+  if constexpr (TS::NW == 4)
+    mainloop_w4<E, TS, KT>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, p.ks, acc);
+  else
+    mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
 
   if constexpr (OS == 2) {
     // 16-bit outputs: stage the tile in LDS, then 16-byte coalesced stores.
@@ -119,8 +122,8 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
     epilogue_linear<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
                               [&](int r, int cc, float v) { put_out<O>(smem + r * pitch + cc * OS, v); });
     __syncthreads();
-    store_staged(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo, row_end - row0,
-                 col0 * OS, p.n * OS, p.store_wt != 0);
+    store_staged<TS::NT>(smem, pitch, TS::BN * OS, TS::BM, p.out + row0 * p.ldo, p.ldo,
+                         row_end - row0, col0 * OS, p.n * OS, p.store_wt != 0);
   } else {
     // 32-bit test outputs: stored straight from the accumulator layout.
     char* base = p.out + row0 * p.ldo + col0 * OS;
@@ -159,8 +162,10 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
 // instead (units n_full.. map to the two row halves of tiles n_full..): the
 // round then ends after a 128-row tile's time. Each half still sums all of K
 // once, so results do not depend on the split.
-template <Elem E, bool BT, class TS, Out O>
-__global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p) {
+// KT: the K extent of a shard may end inside a stage (four-wave tiles
+// only; the eight-wave loop always checks).
+template <Elem E, bool BT, class TS, Out O, bool KT>
+__global__ __launch_bounds__(TS::NT, 1) void chunked_gemm_kernel(ChunkedArgs p) {
   constexpr int kSmem = chunked_smem<TS, OutInfo<O>::bytes>();
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   lds_t* smem = (lds_t*)smem_raw;
@@ -169,11 +174,11 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
     using TH = Tile<128, TS::BN, TS::WM, TS::WN>;
     if (u >= p.n_full) {
       const int v = u - p.n_full;
-      chunked_tile<E, BT, TH, O>(p, smem, p.n_full + (v >> 1), v & 1, 1u);
+      chunked_tile<E, BT, TH, O, KT>(p, smem, p.n_full + (v >> 1), v & 1, 1u);
       return;
     }
   }
-  chunked_tile<E, BT, TS, O>(p, smem, u, 0, 2u);
+  chunked_tile<E, BT, TS, O, KT>(p, smem, u, 0, 2u);
 }
 
 // ---------------------------------------------------------------- host side
@@ -181,7 +186,14 @@ __global__ __launch_bounds__(kThreads, 1) void chunked_gemm_kernel(ChunkedArgs p
 
 template <Elem E, bool BT, class TS, Out O>
 static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s) {
-  hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TS, O>), dim3(blocks), dim3(kThreads), 0, s, a);
+  if constexpr (TS::NW == 4) {
+    if (a.ks.k % (kKBytes / ElemInfo<E>::bytes) == 0) {
+      hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TS, O, false>), dim3(blocks), dim3(TS::NT), 0,
+                         s, a);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((chunked_gemm_kernel<E, BT, TS, O, true>), dim3(blocks), dim3(TS::NT), 0, s, a);
   return hipGetLastError();
 }
 
@@ -197,7 +209,7 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   if (in_dtype == MC2_BF16)
     return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
                                 : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
-  if constexpr (TS::BN != 256) {
+  if constexpr (TS::BN != 256 || TS::NW == 4) {
     return hipErrorInvalidValue;
   } else {
     switch (out_dtype) {
@@ -316,7 +328,8 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   if (shape == 2)
     e = dispatch_chunked<false, TileN>(in_dtype, out_dtype, a, (int)blocks, stream);
   else if (tall)
-    e = x2_trans ? dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)
+    e = x2_trans ? (es == 2 ? dispatch_chunked<true, TileW>(in_dtype, out_dtype, a, (int)blocks, stream)
+                            : dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream))
                  : dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
   else
     e = x2_trans ? dispatch_chunked<true, TileM>(in_dtype, out_dtype, a, (int)blocks, stream)

@@ -5,6 +5,7 @@
 
 #include "../../include/mc2.h"
 #include "gemm_core.hpp"
+#include "gemm_core_w4.hpp"
 #include "mc2_host.hpp"
 
 namespace mc2 {
@@ -99,6 +100,7 @@ __device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
 using TileL = Tile<256, 256, 2, 4>;  // wave sub-tile 128 x 64
 using TileM = Tile<128, 256, 2, 4>;  // wave sub-tile 64 x 64, for small tile counts
 using TileN = Tile<256, 192, 2, 4>;  // wave sub-tile 128 x 48: tile counts that fill whole rounds
+using TileW = Tile<256, 256, 2, 2>;  // four waves of 128 x 128, operands K-contiguous (B as (n, k))
 
 inline bool valid_world(int W) { return W == 1 || W == 2 || W == 4 || W == 8 || W == 16 || W == 32; }
 
