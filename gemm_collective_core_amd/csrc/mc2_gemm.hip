@@ -209,7 +209,7 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   if (in_dtype == MC2_BF16)
     return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
                                 : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
-  if constexpr (TS::BN != 256 || TS::NW == 4) {
+  if constexpr (TS::BN != 256 || (TS::NW == 4 && TS::BM == 256)) {
     return hipErrorInvalidValue;
   } else {
     switch (out_dtype) {
@@ -332,7 +332,7 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
                             : dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream))
                  : dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
   else
-    e = x2_trans ? dispatch_chunked<true, TileM>(in_dtype, out_dtype, a, (int)blocks, stream)
+    e = x2_trans ? dispatch_chunked<true, TileWM>(in_dtype, out_dtype, a, (int)blocks, stream)
                  : dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
   return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
