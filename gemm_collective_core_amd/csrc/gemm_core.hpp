@@ -1,7 +1,7 @@
 // Device building blocks of the MFMA contraction kernels (gfx950).
 //
 // Workgroup: 8 waves = 512 threads, two waves per SIMD, computing a BM x BN
-// output tile (256 x 256, 128 x 256, or 256 x 192 for 16-bit inputs); wave
+// output tile (256 x 256 or 128 x 256); wave
 // (wm, wn) owns a WTM x WTN sub-tile. Two waves per SIMD let one wave's MFMAs run while the other waits
 // on its operand reads or on a load instruction the memory pipeline has not
 // yet taken.
@@ -48,8 +48,7 @@
 //    i mod 8 of the pieces read by lanes 2e + i/8 (e = 0..7). So lane j reads
 //    k row 4h + (j >> 2), columns 4(j & 3).. (16-bit) or k row 8h + (j >> 1),
 //    columns 8(j & 1).. (8-bit), and lane i receives consecutive k values of
-//    column i. Rows are swizzled in 32-byte pairs (16-bit; XOR for 512-byte
-//    rows, a rotation for the 384-byte rows of 192-column tiles) or 16-byte
+//    column i. Rows are swizzled in 32-byte pairs (16-bit, XOR) or 16-byte
 //    chunks (8-bit) so that the rows one read touches sit on distinct banks.
 #pragma once
 
@@ -74,7 +73,7 @@ struct Tile {
   static constexpr int WTM = BM / WM, WTN = BN / WN;
   static constexpr int FM = WTM / 16, FN = WTN / 16;
   static_assert(FM * 16 * WM == BM && FN * 16 * WN == BN, "tile not divisible");
-  static_assert((BN == 256 || BN == 192) && BM % 64 == 0, "tile shapes of the load mapping");
+  static_assert(BN == 256 && BM % 64 == 0, "tile shapes of the load mapping");
   static constexpr int kABytes = BM * kKBytes;
   static constexpr int kBBytes = BN * kKBytes;  // same size in both B layouts
   static constexpr int kStageBytes = kABytes + kBBytes;
@@ -129,29 +128,15 @@ __device__ __forceinline__ int row_off(int r, int c) {
 __device__ __forceinline__ int kmaj_swz16(int kr) { return (kr & 3) | (((kr >> 3) & 1) << 2); }
 
 // Position of 32-byte pair p (16 columns) in 16-bit k row kr of a tile BN
-// columns wide, and its inverse. 512-byte rows: XOR with kmaj_swz16. 384-byte
-// rows (12 pairs): rotation by ((kr >> 1) & 1) | ((kr >> 3) & 1) << 1. A row
-// of 384 bytes moves the bank by 4 32-byte groups per row (12 mod 8), so the
-// 8 rows one half-wave of a transposing read touches (kr & 3 and bit 3 of kr
-// taking all 8 values) land on 4 * (kr & 1) + rotation + p mod 8: all 8
-// groups, once each.
+// (256) columns wide, and its inverse: XOR with kmaj_swz16 (an involution).
 template <int BN>
 __device__ __forceinline__ int kmaj_pos16(int p, int kr) {
-  if constexpr (BN == 256) {
-    return p ^ kmaj_swz16(kr);
-  } else {
-    const int q = p + (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
-    return q < 12 ? q : q - 12;
-  }
+  static_assert(BN == 256, "512-byte k rows");
+  return p ^ kmaj_swz16(kr);
 }
 template <int BN>
 __device__ __forceinline__ int kmaj_unpos16(int pp, int kr) {
-  if constexpr (BN == 256) {
-    return pp ^ kmaj_swz16(kr);
-  } else {
-    const int q = pp - (((kr >> 1) & 1) | (((kr >> 3) & 1) << 1));
-    return q >= 0 ? q : q + 12;
-  }
+  return kmaj_pos16<BN>(pp, kr);
 }
 __device__ __forceinline__ int kmaj_swz8(int kr) { return (kr & 7) | (((kr >> 4) & 1) << 3); }
 
@@ -296,7 +281,6 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
   constexpr int NA = TS::BM / 64;         // A loads per wave per stage
   constexpr int NB = TS::BN / 64;         // B loads per wave per stage
   static_assert(TS::NW == 8, "the eight-wave schedule");
-  static_assert(TS::BN == 256 || (ES == 2 && !BT), "192-column tiles: 16-bit row-major B only");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;

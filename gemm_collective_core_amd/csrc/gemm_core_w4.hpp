@@ -97,13 +97,19 @@ constexpr int load_slot_index(int q, int a, int span, int nl) {
   return -1;
 }
 
+// BT: B given as (n, k) (K-contiguous, like A); otherwise row-major (k, n),
+// kept k-major in LDS and read with the transposing LDS reads (16-bit only),
+// `colmap(c)` giving the global column of tile column c (a multiple of 8).
 // KTAIL: the shard's K extent may end inside a stage, so every load checks
 // its lanes against the K values left (lanes past the end load zeros);
 // without it (K a multiple of the stage) the loads carry no per-lane check.
-template <Elem E, class TS, bool KTAIL>
+//
+// LDS: A of stage 0, B of stage 0, B of stage 1, A of stage 1, so that the
+// two B buffers lie within one immediate offset of each other.
+template <Elem E, bool BT, class TS, bool KTAIL, class ColMap>
 __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                             int64_t row_last, const BDesc& B, int64_t col0,
-                                            const KSpan& ks,
+                                            const ColMap& colmap, const KSpan& ks,
                                             typename Mma<E>::acc_t (&acc)[TS::FM][TS::FN]) {
   constexpr int ES = ElemInfo<E>::bytes;
   constexpr int KE = kKBytes / ES;  // K values per stage
@@ -112,8 +118,10 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   constexpr int NA = TS::BM / 32;   // A loads per wave per stage (8 rows each, 4 waves)
   constexpr int NB = TS::BN / 32;   // B loads per wave per stage
   constexpr int NL = NA + NB;
-  constexpr int NR = FM + FN;       // operand reads per wave per k-step
+  constexpr int NBR = BT ? FN : 2 * FN;  // B operand reads per k-step (8 bytes each if !BT)
+  constexpr int NR = FM + NBR;      // operand reads per wave per k-step
   static_assert(TS::NW == 4 && TS::BN == 256, "four waves, 256-column tiles");
+  static_assert(BT || ES == 2, "row-major B: 16-bit elements");
   static_assert(NL <= 63, "vmcnt range of the prologue");
   constexpr int MM = FM * FN;       // MFMA slots per k-step
   // Slots q = 0 .. 2 MM - 1 of a stage (k-step 1 from MM on), one MFMA each:
@@ -125,7 +133,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   //   kBarB         wait for this wave's loads of the next stage, barrier;
   //   after kBarB   the next stage's k-step-0 operand reads.
   constexpr int kBarA = NR + 4;
-  constexpr int kBarB = 2 * MM - NR - 8;
+  constexpr int kBarB = 2 * MM - NR - 4;
   constexpr int kLSpan = kBarB - kBarA - 1;
   static_assert(kLSpan >= NL && kBarB + NR < 2 * MM, "slots for the loads and the reads");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -139,26 +147,42 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   // Per-lane offsets of this wave's loads: lane -> row (lane >> 3) of the 8
   // rows a load writes, physical chunk lane & 7, holding logical chunk
   // (lane & 7) ^ swizzle.
+  // Row-major B: a load writes 1 KiB linearly over consecutive k rows of BN
+  // columns (512 bytes each); lane -> k row, 16-byte piece of it, holding the
+  // columns of the 32-byte pair the k-major swizzle puts there.
   uint32_t l_off[NL];
   int l_key[NL];
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const bool isa = j < NA;
-    const int r = 8 * ((isa ? NA : NB) * wave + (isa ? j : j - NA)) + (lane >> 3);
-    const int c = (row_off(r, lane & 7) - r * kKBytes) >> 4;
-    if (isa) {
-      int64_t gr = row0 + r;
-      gr = gr < row_last ? gr : row_last;
-      l_off[j] = static_cast<uint32_t>((gr - row0) * lda + c * 16);
+    if (isa || BT) {
+      const int r = 8 * ((isa ? NA : NB) * wave + (isa ? j : j - NA)) + (lane >> 3);
+      const int c = (row_off(r, lane & 7) - r * kKBytes) >> 4;
+      if (isa) {
+        int64_t gr = row0 + r;
+        gr = gr < row_last ? gr : row_last;
+        l_off[j] = static_cast<uint32_t>((gr - row0) * lda + c * 16);
+      } else {
+        int64_t gc = col0 + r;
+        gc = gc < B.n - 1 ? gc : B.n - 1;
+        l_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
+      }
+      l_key[j] = c * CE;
     } else {
-      int64_t gc = col0 + r;
-      gc = gc < B.n - 1 ? gc : B.n - 1;
-      l_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
+      const int o = (NB * wave + (j - NA)) * 1024 + 16 * lane;
+      const int kr = o / (TS::BN * 2);
+      const int pc = (o - kr * (TS::BN * 2)) >> 4;
+      const int ch = (kmaj_unpos16<TS::BN>(pc >> 1, kr) << 1) | (pc & 1);
+      l_off[j] = static_cast<uint32_t>(kr * B.ld + colmap(ch * 8) * 2);
+      l_key[j] = kr;
     }
-    l_key[j] = c * CE;
   }
   const char* a_base = A + row0 * lda;
-  const char* b_base = B.base + col0 * B.ld;
+  const char* b_base = BT ? B.base + col0 * B.ld : B.base;
+  // LDS regions: A of stage p at a_lds(p), B of stage p at b_lds(p)
+  constexpr int kA1 = TS::kABytes + 2 * TS::kBBytes;
+  auto a_lds = [](int p) { return p ? kA1 : 0; };
+  auto b_lds = [](int p) { return TS::kABytes + p * TS::kBBytes; };
 
   // Loads of stage it: the buffer resources are formed once per stage; a
   // stage past the last one gets resources of no records, so its loads (the
@@ -167,7 +191,8 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   struct StageLd {
     __amdgpu_buffer_rsrc_t ra, rb;
     int kleft;  // K values left in this shard (clamped)
-    lds_t* st;
+    lds_t* st;   // A destination
+    lds_t* stb;  // B destination
   };
   // Stages are loaded in order; (lw, lkt) is the shard and K stage of the
   // next stage to load, advanced with scalar adds (no division per stage).
@@ -177,12 +202,14 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     const int64_t kdone = static_cast<int64_t>(lkt) * KE;
     const int64_t kl = ks.k - kdone;
     s.kleft = static_cast<int>(kl < (1 << 30) ? kl : (1 << 30));
-    s.st = smem + (ld_it & 1) * TS::kStageBytes;
+    s.st = smem + ((ld_it & 1) ? kA1 : 0);
+    s.stb = smem + TS::kABytes + (ld_it & 1) * TS::kBBytes;
     const int nrec = ld_it < ks.niters ? 0x7ffffff0 : 0;
     s.ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(a_base + lw * ks.a_shard + kdone * ES), 0, nrec, kBufFlags);
     s.rb = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(b_base + lw * ks.b_shard + kdone * ES), 0, nrec, kBufFlags);
+        const_cast<char*>(b_base + lw * ks.b_shard + (BT ? kdone * ES : kdone * B.ld)), 0, nrec,
+        kBufFlags);
     ++ld_it;
     if (++lkt == ks.ktiles) {
       lkt = 0;
@@ -196,7 +223,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     if (j < NA)
       dma16(s.ra, s.st + 8 * (NA * wave + j) * kKBytes, off);
     else
-      dma16(s.rb, s.st + TS::kABytes + 8 * (NB * wave + (j - NA)) * kKBytes, off);
+      dma16(s.rb, s.stb + 8 * (NB * wave + (j - NA)) * kKBytes, off);
   };
 
   // LDS read addresses of the wave's first fragment (row wrow0 + (lane & 15)
@@ -209,25 +236,71 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
 #pragma unroll
     for (int k2 = 0; k2 < 2; ++k2) {
       const int ch = k2 * 4 + (lane >> 4);
-      adA[p][k2] = s0 + p * TS::kStageBytes + row_off(wrow0 + (lane & 15), ch);
-      adB[p][k2] = s0 + p * TS::kStageBytes + TS::kABytes + row_off(wcol0 + (lane & 15), ch);
+      adA[p][k2] = s0 + a_lds(p) + row_off(wrow0 + (lane & 15), ch);
+      adB[p][k2] = s0 + b_lds(p) + row_off(wcol0 + (lane & 15), ch);
     }
+  // Row-major B: the transposing read of half h of fragment fn, k-step k2,
+  // buffer p, reads lane j of group g at k row 32 k2 + 8 g + 4 h + (j >> 2),
+  // 32-byte pair (wcol0 / 16 + fn) ^ swizzle, byte 8 (j & 3). The swizzle
+  // depends only on the lane ((j >> 2) and the parity of g), and the wave's
+  // pairs are wcol0 / 16 + 0..7 with wcol0 / 16 in {0, 8}, so the pair is
+  // wcol0 / 16 | (fn ^ swizzle): one address register per fragment, with
+  // buffer, k-step and half in the immediate offset.
+  uint32_t adT[BT ? 1 : FN];
+  if constexpr (!BT) {
+    const int j = lane & 15, g = lane >> 4;
+    const int swz = (j >> 2) | ((g & 1) << 2);
+    const uint32_t base = s0 + TS::kABytes + (g * 8 + (j >> 2)) * (TS::BN * 2) + ((j & 3) << 3);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      adT[fn] = base + ((((wcol0 >> 4) | (fn ^ swz))) << 5);
+  }
 
-  u32x4_t a0[FM], b0[FN], a1[FM], b1[FN];
-  // operand read number i of a k-step: B fragments first, then A
-  auto read_op = [&](auto I, uint32_t adA_, uint32_t adB_, u32x4_t (&a)[FM], u32x4_t (&b)[FN]) {
-    constexpr int i = decltype(I)::value;
-    if constexpr (i < FN)
-      b[i] = lds_rd128_at<i * 16 * kKBytes>(adB_);
-    else
-      a[i - FN] = lds_rd128_at<(i - FN) * 16 * kKBytes>(adA_);
+  // A fragments: 16-byte reads; B fragments: 16-byte reads (B as (n, k)) or
+  // two 8-byte transposing reads whose halves form the MFMA operand after
+  // the wait (so no register copy can read a half still in flight).
+  struct BOps {
+    u32x4_t q[BT ? FN : 1];
+    u32x2_t h[BT ? 1 : FN][2];
+    __device__ __forceinline__ u32x4_t get(int fn) const {
+      if constexpr (BT) return q[fn];
+      else return u32x4_t{h[fn][0][0], h[fn][0][1], h[fn][1][0], h[fn][1][1]};
+    }
   };
-  auto tie = [&](u32x4_t (&a)[FM], u32x4_t (&b)[FN]) {
+  u32x4_t a0[FM], a1[FM];
+  BOps b0, b1;
+  // operand read number i of k-step K2 from buffer P: B reads first, then A
+  auto read_op = [&](auto I, auto Pc, auto K2c, u32x4_t (&a)[FM], BOps& b) {
+    constexpr int i = decltype(I)::value, P = decltype(Pc)::value, K2 = decltype(K2c)::value;
+    if constexpr (i >= NBR) {
+      a[i - NBR] = lds_rd128_at<(i - NBR) * 16 * kKBytes>(adA[P][K2]);
+    } else if constexpr (BT) {
+      b.q[i] = lds_rd128_at<i * 16 * kKBytes>(adB[P][K2]);
+    } else {
+      constexpr int fn = i / 2, h = i % 2;
+      constexpr int off = P * TS::kBBytes + (32 * K2 + 4 * h) * TS::BN * 2;
+      static_assert(off < 65536, "ds_read offset field");
+      const uint32_t addr = adT[fn];
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(b.h[fn][h]) : "v"(addr), "i"(off) : "memory");
+    }
+  };
+  auto tie = [&](u32x4_t (&a)[FM], BOps& b) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a[i]));
+    if constexpr (BT) {
 #pragma unroll
-    for (int i = 0; i < FN; ++i) asm volatile("" : "+v"(b[i]));
+      for (int i = 0; i < FN; ++i) asm volatile("" : "+v"(b.q[i]));
+    } else {
+#pragma unroll
+      for (int i = 0; i < FN; ++i) {
+        asm volatile("" : "+v"(b.h[i][0]));
+        asm volatile("" : "+v"(b.h[i][1]));
+      }
+    }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   const int n = ks.niters;  // at least 1
   StageLd nx;
@@ -240,7 +313,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     for (int j = 0; j < NL; ++j) issue_j(nx, j);
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");  // stage 0 has landed
     bar_sync();
-    sfor<NR>([&](auto I) { read_op(I, adA[0][0], adB[0][0], a0, b0); });
+    sfor<NR>([&](auto I) { read_op(I, I0{}, I0{}, a0, b0); });
   }
 
   // One stage from buffer P; the first stage starts the accumulators.
@@ -255,14 +328,14 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       if constexpr (q == MM) tie(a1, b1);
       if constexpr (q < MM) {
         if constexpr (FIRST)
-          MmaA<E>::init(acc[fm][fn], a0[fm], b0[fn]);
+          MmaA<E>::init(acc[fm][fn], a0[fm], b0.get(fn));
         else
-          MmaA<E>::acc(acc[fm][fn], a0[fm], b0[fn]);
+          MmaA<E>::acc(acc[fm][fn], a0[fm], b0.get(fn));
       } else {
-        MmaA<E>::acc(acc[fm][fn], a1[fm], b1[fn]);
+        MmaA<E>::acc(acc[fm][fn], a1[fm], b1.get(fn));
       }
       if constexpr (q < NR) {
-        read_op(std::integral_constant<int, q>{}, adA[P][1], adB[P][1], a1, b1);
+        read_op(std::integral_constant<int, q>{}, Pc, I1{}, a1, b1);
       } else if constexpr (q == kBarA) {
         lgkm_wait(0);  // every read of this stage's buffer is done
         bar_sync();    // ... by every wave: the buffer may be refilled
@@ -277,13 +350,12 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       } else if constexpr (q > kBarB && (q - kBarB - 1) < NR) {
         // the next stage's k-step-0 operands (after the last stage: reads of
         // a buffer nobody writes any more, never used)
-        read_op(std::integral_constant<int, q - kBarB - 1>{}, adA[1 - P][0], adB[1 - P][0], a0, b0);
+        read_op(std::integral_constant<int, q - kBarB - 1>{}, std::integral_constant<int, 1 - P>{},
+                I0{}, a0, b0);
       }
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
   using T = std::true_type;
   using F = std::false_type;
   stage(I0{}, T{}, 0);

@@ -112,7 +112,7 @@ __device__ __forceinline__ void chunked_tile(const ChunkedArgs& p, lds_t* smem, 
   BDesc bd{p.B, p.ldb, p.n};
   PlainCols cm{col0, p.n - 16 / ElemInfo<E>::bytes};
   if constexpr (TS::NW == 4)
-    mainloop_w4<E, TS, KT>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, p.ks, acc);
+    mainloop_w4<E, BT, TS, KT>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
   else
     mainloop<E, BT, TS>(smem, p.A, p.lda, row0, row_end - 1, bd, col0, cm, p.ks, acc);
 
@@ -198,8 +198,8 @@ static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s
 }
 
 // Instantiated combinations: F16 -> {F16, F32}; BF16 -> {BF16, F32};
-// I8 -> {BF16, F16, F32, I32} (not with 192-column tiles, which take 16-bit
-// row-major B only).
+// I8 -> {BF16, F16, F32, I32} (eight-wave tiles, and four-wave 128-row tiles
+// with B given (n, k)).
 template <bool BT, class TS>
 static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArgs& a, int blocks,
                                    hipStream_t s) {
@@ -209,7 +209,7 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   if (in_dtype == MC2_BF16)
     return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
                                 : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
-  if constexpr (TS::BN != 256 || (TS::NW == 4 && TS::BM == 256)) {
+  if constexpr (TS::NW == 4 && (TS::BM == 256 || !BT)) {
     return hipErrorInvalidValue;
   } else {
     switch (out_dtype) {
@@ -237,12 +237,9 @@ static int64_t chunk_tiles(int64_t sq, int sr, int sub, int bm, int64_t tn) {
 }
 
 // Tile shape for a problem: 0 = 256 x 256 (a last round at most half full
-// runs as 128-row halves), 1 = 128 x 256, 2 = 256 x 192 (16-bit inputs with
-// row-major B only). Costs are counted in quarter rounds of 256 x 256 tiles;
-// a 128 x 256 or a 256 x 192 tile counts 3. A 256 x 192 tile is taken only
-// where its rounds are cheaper than both others (8192 x 3072 on 256 CUs: 512
-// tiles in 2 rounds, against 384 whole tiles in 1.5 rounds).
-static int tile_shape(int64_t sq, int sr, int sub, int64_t n, int W, bool narrow_ok) {
+// runs as 128-row halves), 1 = 128 x 256. Costs are counted in quarter
+// rounds of 256 x 256 tiles; a 128 x 256 tile counts 3.
+static int tile_shape(int64_t sq, int sr, int sub, int64_t n, int W) {
   const int64_t cus = num_cus();
   const int64_t tn = (n + 255) / 256;
   const int64_t tl = chunk_tiles(sq, sr, sub, 256, tn) * W;
@@ -250,11 +247,6 @@ static int tile_shape(int64_t sq, int sr, int sub, int64_t n, int W, bool narrow
   const int64_t rl = (tl + cus - 1) / cus, rm = (tm + cus - 1) / cus;
   const int64_t cost_l = half_tail(tl, cus) ? 4 * (rl - 1) + 3 : 4 * rl;
   const int64_t cost_m = 3 * rm;
-  if (narrow_ok) {
-    const int64_t tnn = chunk_tiles(sq, sr, sub, 256, (n + 191) / 192) * W;
-    const int64_t cost_n = 3 * ((tnn + cus - 1) / cus);
-    if (cost_n < cost_l && cost_n < cost_m) return 2;
-  }
   return cost_l <= cost_m ? 0 : 1;
 }
 
@@ -289,10 +281,9 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   a.sub = sub;
   a.sq = a.mc / sub;
   a.sr = static_cast<int>(a.mc % sub);
-  const int shape = tile_shape(a.sq, a.sr, sub, n, W, es == 2 && !x2_trans);
-  const bool tall = shape != 1;
+  const bool tall = tile_shape(a.sq, a.sr, sub, n, W) == 0;
   const int BM = tall ? TileL::BM : TileM::BM;
-  const int BN = shape == 2 ? TileN::BN : TileL::BN;
+  const int BN = TileL::BN;
   a.tiles_m1 = static_cast<int>((a.sq + BM) / BM);
   a.tiles_m0 = static_cast<int>((a.sq + BM - 1) / BM);
   a.tiles_n = static_cast<int>((n + BN - 1) / BN);
@@ -319,21 +310,26 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
   // A last round filled to at most half runs as half tiles (see the kernel).
   int64_t blocks = tiles;
   a.n_full = static_cast<int>(tiles);
-  if (shape == 0 && half_tail(tiles, num_cus())) {
+  if (tall && half_tail(tiles, num_cus())) {
     const int64_t rem = tiles % num_cus();
     a.n_full = static_cast<int>(tiles - rem);
     blocks = tiles + rem;
   }
+  // 16-bit inputs run the four-wave loop in both B layouts; int8 with B
+  // given (n, k) runs it in 128-row tiles (a load-path-bound share that never
+  // fills enough 256-row tiles); int8 with row-major B runs the eight-wave loop.
   hipError_t e;
-  if (shape == 2)
-    e = dispatch_chunked<false, TileN>(in_dtype, out_dtype, a, (int)blocks, stream);
+  if (tall && es == 2)
+    e = x2_trans ? dispatch_chunked<true, TileW>(in_dtype, out_dtype, a, (int)blocks, stream)
+                 : dispatch_chunked<false, TileW>(in_dtype, out_dtype, a, (int)blocks, stream);
   else if (tall)
-    e = x2_trans ? (es == 2 ? dispatch_chunked<true, TileW>(in_dtype, out_dtype, a, (int)blocks, stream)
-                            : dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream))
+    e = x2_trans ? dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)
                  : dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
-  else
+  else if (x2_trans || es == 2)
     e = x2_trans ? dispatch_chunked<true, TileWM>(in_dtype, out_dtype, a, (int)blocks, stream)
-                 : dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
+                 : dispatch_chunked<false, TileWM>(in_dtype, out_dtype, a, (int)blocks, stream);
+  else
+    e = dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
   return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 

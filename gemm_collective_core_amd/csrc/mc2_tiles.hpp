@@ -99,7 +99,6 @@ __device__ __forceinline__ int xcd_tile(int b, int round, int nblocks) {
 
 using TileL = Tile<256, 256, 2, 4>;  // wave sub-tile 128 x 64
 using TileM = Tile<128, 256, 2, 4>;  // wave sub-tile 64 x 64, for small tile counts
-using TileN = Tile<256, 192, 2, 4>;  // wave sub-tile 128 x 48: tile counts that fill whole rounds
 using TileW = Tile<256, 256, 2, 2>;  // four waves of 128 x 128, operands K-contiguous (B as (n, k))
 using TileWM = Tile<128, 256, 2, 2>; // four waves of 64 x 128, for small tile counts
 

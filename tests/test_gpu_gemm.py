@@ -190,13 +190,12 @@ def test_last_round_as_half_tiles():
 
 
 @pytest.mark.parametrize("dtype", [wl.F16, wl.BF16])
-def test_192_column_tiles_full_rounds(dtype):
-    """Shapes whose 256 x 192 tiles fill whole dispatch rounds on 256 CUs, as
-    the 8192 x 3072 share's do: W = 8 chunks of 1000 rows (ragged 256-row
-    tiles), n = 1400 (a last tile of 56 columns), k = 776 (a K tail). Every
-    element against the oracle, with ready flags, in reduce-scatter and
-    AllGatherMatmul order; then the simulated W = 2 reduce-scatter of two
-    shards of k = 392 (chunks of 4000 rows, again 256 tiles)."""
+def test_ragged_chunks_columns_and_k(dtype):
+    """W = 8 chunks of 1000 rows (ragged 256-row tiles), n = 1400 (a last
+    column tile of 120 columns), k = 776 (a K tail): every element against the
+    oracle, with ready flags, in reduce-scatter and AllGatherMatmul order and
+    in both x2 layouts; then the simulated W = 2 reduce-scatter of two shards
+    of k = 392."""
     W = 8
     t = "bf16" if dtype == wl.BF16 else None
     d = wl.gemm_inputs(29, W * 1000, 776, 1400, dtype, std=1.0)
@@ -207,6 +206,10 @@ def test_192_column_tiles_full_rounds(dtype):
     assert flags.cpu().tolist() == [4] * W
     assert counters.cpu().tolist() == [0] * W
     assert_tol(to_f64(out), ref, f"rs {dtype}")
+    dn = wl.x2_as_nk(d)
+    out = _run_rs(dn, W, 3, flags=(flags, counters), epoch=5)
+    assert flags.cpu().tolist() == [5] * W
+    assert_tol(to_f64(out), ref, f"rs {dtype} x2 (n, k)")
     out = mc2.mc2_ag_mm_local(to_dev(d["x1"], t), to_dev(d["x2"], t), W, 5,
                               ready_flags=flags, flag_counters=counters, epoch=6)
     torch.cuda.synchronize()
@@ -216,11 +219,11 @@ def test_192_column_tiles_full_rounds(dtype):
     assert_tol(to_f64(_run_rs(d2, 2, 0)), _oracle_rs(d2, 2), f"sim rs {dtype}")
 
 
-def test_192_column_tiles_other_paths():
-    """Other paths of a 192-column-tile launch (all three shapes select them on
-    256 CUs): bias with the test-only fp32 output; comm_turn 3 pieces with
-    their own flags, bit-identical to the unsplit call (W = 2 chunks of 3000
-    rows, pieces of 1000); input flags, all present."""
+def test_bias_pieces_and_inflags_on_ragged_chunks():
+    """Other paths on the same ragged launch shapes: bias with the test-only
+    fp32 output; comm_turn 3 pieces with their own flags, bit-identical to the
+    unsplit call (W = 2 chunks of 3000 rows, pieces of 1000); input flags,
+    all present."""
     W = 8
     d = wl.gemm_inputs(31, W * 1000, 392, 1400, wl.BF16, std=1.0, bias=True)
     out = _run_rs(d, W, 2, out_dtype="f32", bias=d["bias"])
