@@ -136,7 +136,7 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (
       }
     }
     __syncthreads();
-    for (int q = tid; q < HR * CPR; q += kThreads) {
+    for (int q = tid; q < HR * CPR; q += TS::NT) {
       const int r = q / CPR, c8 = q - r * CPR;
       const int64_t row = half * HR + r;
       const int64_t col = ocol0 + c8 * 8;
@@ -176,8 +176,10 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (
 template <class TS>
 using TileHalf = Tile<TS::BM / 2, TS::BN, TS::WM, TS::WN>;
 
-template <class TS, int MODE, bool BT>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p) {
+// KT: the contraction length may end inside a stage (four-wave tiles only;
+// the eight-wave loop always checks).
+template <class TS, int MODE, bool BT, bool KT>
+__global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) {
   constexpr bool GLU = MODE == kSwiglu;
   static_assert(!(GLU && BT), "the interleaved gate / up columns need row-major weights");
   constexpr int kSmem = grouped_smem<TS, MODE>();
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
   if (tid == 0) { s_base = 0; s_bad = 0; }
   __syncthreads();
   int64_t part = 0;
-  for (int e = tid; e < first; e += kThreads) {
+  for (int e = tid; e < first; e += TS::NT) {
     const int32_t v = p.send_counts[e];
     if (v < 0) s_bad = 1;
     part += v;
@@ -269,10 +271,18 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
     BDesc bd{p.B + g * p.b_group, p.ldb, p.n_b};
     if constexpr (GLU) {
       GluCols cm{ocol0, p.inter, p.n_b - 8};
-      mainloop<Elem::BF16, false, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
+      if constexpr (TSX::NW == 4)
+        mainloop_w4<Elem::BF16, false, TSX, KT>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks,
+                                                acc);
+      else
+        mainloop<Elem::BF16, false, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, 0, cm, ks, acc);
     } else {
       PlainCols cm{ocol0, p.n_b - 8};
-      mainloop<Elem::BF16, BT, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks, acc);
+      if constexpr (TSX::NW == 4)
+        mainloop_w4<Elem::BF16, BT, TSX, KT>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks,
+                                             acc);
+      else
+        mainloop<Elem::BF16, BT, TSX>(smem, p.A, p.lda, arow0, arow_end - 1, bd, ocol0, cm, ks, acc);
     }
     if constexpr (MODE == kSwigluBwd) {
       swiglu_bwd_epilogue<TSX>(smem, acc, p, orow0, arow_end - arow0, ocol0);
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(GroupedArgs p
           acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
           [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
     __syncthreads();
-    store_staged(smem, pitch, OUTC * 2, TSX::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
+    store_staged<TSX::NT>(smem, pitch, OUTC * 2, TSX::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
                  ocol0 * 2, p.n_out * 2);
     __syncthreads();
   };
@@ -666,13 +676,18 @@ using namespace mc2;
 
 namespace mc2 {
 
-using TileG = TileL;
+using TileG = TileW;
 
 template <int MODE, bool BT>
 static int run_grouped(const GroupedArgs& a, int64_t max_tiles, hipStream_t stream) {
   const int64_t grid64 = max_tiles < num_cus() ? max_tiles : num_cus();
   const int grid = static_cast<int>(grid64 > 0 ? grid64 : 1);
-  hipLaunchKernelGGL((grouped_gemm_kernel<TileG, MODE, BT>), dim3(grid), dim3(kThreads), 0, stream,
+  if (a.K % 64 == 0) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<TileG, MODE, BT, false>), dim3(grid), dim3(TileG::NT), 0,
+                       stream, a);
+    return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
+  }
+  hipLaunchKernelGGL((grouped_gemm_kernel<TileG, MODE, BT, true>), dim3(grid), dim3(TileG::NT), 0, stream,
                      a);
   return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
