@@ -13,11 +13,13 @@ _I = C.c_int
 _U32 = C.c_uint32
 SIGNATURES = {
     "mc2_mm_rs_local": (_I, [_P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _I, _P, _P, _P, _I, _P,
-                             _P, _P, _U32, _I, _P]),
+                             _P, _P, _U32, _I, _P, C.c_size_t, _P]),
     "mc2_ag_mm_local": (_I, [_P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P, _P, _P, _P, _U32, _I,
-                             _P]),
+                             _P, C.c_size_t, _P]),
     "mc2_ag_mm_local_inflags": (_I, [_P, _P, _I64, _I64, _I64, _I, _I, _I, _I, _P, _P, _P, _P,
-                                     _U32, _I, _P, _U32, _U32, _P, _P]),
+                                     _U32, _I, _P, _U32, _U32, _P, _P, C.c_size_t, _P]),
+    "mc2_split_workspace_size": (C.c_size_t, []),
+    "mc2_set_split_policy": (_I, [_I]),
     "mc2_mm_ar_workspace_size": (C.c_size_t, [_I64, _I64, _I, _I, _I]),
     "mc2_mm_ar_local": (_I, [_P, _P, _I64, _I64, _I64, _I, _I, _I, _P, _I, _P, _P, C.c_size_t,
                              _P]),

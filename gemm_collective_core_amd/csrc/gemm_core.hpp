@@ -109,7 +109,8 @@ struct KSpan {
   int64_t a_shard;  // bytes between A shards
   int64_t b_shard;  // bytes between B shards
   int ktiles;       // K stages per shard
-  int niters;       // nsim * ktiles
+  int niters;       // end of the stages run: nsim * ktiles, or less for a K part
+  int it0 = 0;      // first stage run (0, or the start of a K part)
 };
 
 // Operand B description for the main loop.
@@ -340,8 +341,9 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
   };
   auto prep = [&](int it) {
     StageLd s;
-    const int w = it / ks.ktiles;
-    const int kt = it - w * ks.ktiles;
+    const int ia = it + ks.it0;
+    const int w = ia / ks.ktiles;
+    const int kt = ia - w * ks.ktiles;
     const int64_t kdone = static_cast<int64_t>(kt) * KE;
     s.kleft = ks.k - kdone;
     s.st = smem + (it & 1) * TS::kStageBytes;
@@ -369,7 +371,7 @@ __device__ __forceinline__ void mainloop(lds_t* smem, const char* A, int64_t lda
     for (int j = 0; j < NA + NB; ++j) issue_j(s, j);
   };
 
-  const int n = ks.niters;
+  const int n = ks.niters - ks.it0;
   constexpr int FM = TS::FM, FN = TS::FN;
   constexpr int NBO = BRegs<BT, FN>::kOps;
   // k-step-1 row followed by the barrier: the middle row for 8 fragment rows,

@@ -194,9 +194,11 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     lds_t* st;   // A destination
     lds_t* stb;  // B destination
   };
-  // Stages are loaded in order; (lw, lkt) is the shard and K stage of the
-  // next stage to load, advanced with scalar adds (no division per stage).
-  int ld_it = 0, lw = 0, lkt = 0;
+  // Stages are loaded in order; ld_it counts the stages loaded and (lw, lkt)
+  // is the shard and K stage of the next one, advanced with scalar adds (no
+  // division per stage). A K part starts at stage ks.it0.
+  int ld_it = 0, lw = ks.it0 / ks.ktiles, lkt = ks.it0 - lw * ks.ktiles;
+  const int n = ks.niters - ks.it0;  // at least 1
   auto prep = [&]() {
     StageLd s;
     const int64_t kdone = static_cast<int64_t>(lkt) * KE;
@@ -204,7 +206,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     s.kleft = static_cast<int>(kl < (1 << 30) ? kl : (1 << 30));
     s.st = smem + ((ld_it & 1) ? kA1 : 0);
     s.stb = smem + TS::kABytes + (ld_it & 1) * TS::kBBytes;
-    const int nrec = ld_it < ks.niters ? 0x7ffffff0 : 0;
+    const int nrec = ld_it < n ? 0x7ffffff0 : 0;
     s.ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(a_base + lw * ks.a_shard + kdone * ES), 0, nrec, kBufFlags);
     s.rb = __builtin_amdgcn_make_buffer_rsrc(
@@ -302,7 +304,6 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
 
-  const int n = ks.niters;  // at least 1
   StageLd nx;
   {
     nx = prep();  // stage 0

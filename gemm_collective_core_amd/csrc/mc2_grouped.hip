@@ -188,6 +188,7 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
   __shared__ int64_t s_gstart[kMaxLocalExperts + 1];
   __shared__ int64_t s_tstart[kMaxLocalExperts + 1];
   __shared__ int64_t s_base;
+  __shared__ int32_t s_cnt[kMaxLocalExperts];
   __shared__ int s_bad;
 
   const int tid = threadIdx.x;
@@ -208,15 +209,22 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
   for (int off = 32; off > 0; off >>= 1) part += __shfl_xor(part, off);
   if ((tid & 63) == 0 && part) atomicAdd(reinterpret_cast<unsigned long long*>(&s_base),
                                          static_cast<unsigned long long>(part));
+  // the counts are read in parallel (one load round trip, not one per
+  // expert), then one thread scans them in shared memory
+  for (int e = tid; e < El; e += TS::NT) {
+    const int32_t rc = p.recv_counts[e];
+    if (rc < 0 || rc != p.send_counts[first + e]) s_bad = 1;
+    s_cnt[e] = rc > 0 ? rc : 0;
+  }
+  __syncthreads();
   if (tid == 0) {
     int64_t g = 0, tt = 0;
     for (int e = 0; e < El; ++e) {
-      const int32_t rc = p.recv_counts[e];
-      if (rc < 0 || rc != p.send_counts[first + e]) s_bad = 1;
+      const int64_t c = s_cnt[e];
       s_gstart[e] = g;
       s_tstart[e] = tt;
-      g += rc > 0 ? rc : 0;
-      tt += ((rc > 0 ? rc : 0) + TS::BM - 1) / TS::BM * tiles_n;
+      g += c;
+      tt += (c + TS::BM - 1) / TS::BM * tiles_n;
     }
     s_gstart[El] = g;
     s_tstart[El] = tt;

@@ -81,6 +81,41 @@ def mc2_version() -> str:
     return _lib.load().mc2_version().decode()
 
 
+MC2_SPLIT_PAIR = 0
+MC2_SPLIT_ALONE = 1
+
+# K-split workspaces handed out by the binding, one per (device, stream): the
+# library leaves their control words zero after every call, and calls on one
+# stream never overlap.
+_split_ws = {}
+
+
+def mc2_split_workspace_size() -> int:
+    return int(_lib.load().mc2_split_workspace_size())
+
+
+def mc2_set_split_policy(policy: int) -> None:
+    _check("mc2_set_split_policy", _lib.load().mc2_set_split_policy(int(policy)))
+
+
+def _split_workspace(dev, split, workspace):
+    """(pointer, bytes) of the K-split workspace: the caller's, none
+    (split=False), or the binding's own for this device and stream."""
+    if not split:
+        return None, 0
+    if workspace is not None:
+        _want(workspace, "workspace", dtype=torch.uint8)
+        if not workspace.is_cuda or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous GPU tensor")
+        return workspace.data_ptr(), workspace.numel()
+    key = (dev.index, _stream(dev))
+    ws = _split_ws.get(key)
+    if ws is None:
+        ws = torch.zeros(mc2_split_workspace_size(), dtype=torch.uint8, device=dev)
+        _split_ws[key] = ws
+    return ws.data_ptr(), ws.numel()
+
+
 def _check_flags(world_size, comm_turn, ready_flags, flag_counters):
     """Flag arrays hold one uint32 per segment: world_size * max(comm_turn, 1).
     The counters live on the GPU; the ready flags on the GPU or in host-pinned
@@ -98,9 +133,12 @@ def _check_flags(world_size, comm_turn, ready_flags, flag_counters):
 
 def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_scale=None,
                     x2_scale=None, out_dtype=None, out=None, ready_flags=None,
-                    flag_counters=None, epoch=0, comm_turn=0):
+                    flag_counters=None, epoch=0, comm_turn=0, split=True, workspace=None):
     """MatmulReduceScatter compute share; x1 (m, k) or stacked (nsim, m, k),
-    x2 (k, n) / (n, k) or stacked. Returns out (m, n)."""
+    x2 (k, n) / (n, k) or stacked. Returns out (m, n). split=False runs a thin
+    last round as half tiles instead of K halves; workspace: a uint8 GPU
+    tensor for the K split (zeroed before its first use), else the binding's
+    own for this stream."""
     if x1.dim() not in (2, 3):
         raise ValueError("x1 must be (m, k) or stacked (nsim, m, k)")
     _want(x1, "x1", dtypes=(torch.float16, torch.bfloat16, torch.int8))
@@ -123,10 +161,12 @@ def mc2_mm_rs_local(x1, x2, world_size, rank, *, x2_trans=False, bias=None, x1_s
     _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype, device=dev)
+    ws, ws_bytes = _split_workspace(dev, split, workspace)
     st = _lib.load().mc2_mm_rs_local(
         x1.data_ptr(), x2.data_ptr(), m, k, n, world_size, rank, nsim, int(bool(x2_trans)),
         _CODES[x1.dtype], _ptr(bias), _ptr(x1_scale), _ptr(x2_scale), _CODES[out_dtype],
-        out.data_ptr(), _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, _stream(dev))
+        out.data_ptr(), _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, ws, ws_bytes,
+        _stream(dev))
     _check("mc2_mm_rs_local", st)
     return out
 
@@ -149,17 +189,20 @@ def _check_ag(x_gathered, x2, world_size, x2_trans, bias, out):
 
 
 def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=None, out=None,
-                    ready_flags=None, flag_counters=None, epoch=0, comm_turn=0):
-    """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out."""
+                    ready_flags=None, flag_counters=None, epoch=0, comm_turn=0, split=True,
+                    workspace=None):
+    """AllGatherMatmul compute share; x_gathered (W*m_c, k). Returns out.
+    split / workspace as for mc2_mm_rs_local."""
     M, k, n = _check_ag(x_gathered, x2, world_size, x2_trans, bias, out)
     dev = _dev(x_gathered, x2, bias, out, flag_counters)
     _check_flags(world_size, comm_turn, ready_flags, flag_counters)
     if out is None:
         out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
+    ws, ws_bytes = _split_workspace(dev, split, workspace)
     st = _lib.load().mc2_ag_mm_local(
         x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
         int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
-        _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, _stream(dev))
+        _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, ws, ws_bytes, _stream(dev))
     _check("mc2_ag_mm_local", st)
     return out
 
@@ -167,7 +210,7 @@ def mc2_ag_mm_local(x_gathered, x2, world_size, rank, *, x2_trans=False, bias=No
 def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch, *,
                             spin_limit=1 << 24, x2_trans=False, bias=None, out=None,
                             ready_flags=None, flag_counters=None, epoch=0, dev_err=None,
-                            comm_turn=0):
+                            comm_turn=0, split=True, workspace=None):
     """mc2_ag_mm_local whose tiles wait until in_flags[g] == in_epoch before
     reading segment g of a gathered chunk other than the own one. in_flags:
     world_size * max(comm_turn, 1) int32 on the GPU or in host-pinned memory."""
@@ -182,11 +225,12 @@ def mc2_ag_mm_local_inflags(x_gathered, x2, world_size, rank, in_flags, in_epoch
     dev = _dev(x_gathered, x2, bias, out, flag_counters, dev_err)
     if out is None:
         out = torch.empty((M, n), dtype=x_gathered.dtype, device=dev)
+    ws, ws_bytes = _split_workspace(dev, split, workspace)
     st = _lib.load().mc2_ag_mm_local_inflags(
         x_gathered.data_ptr(), x2.data_ptr(), M // world_size, k, n, world_size, rank,
         int(bool(x2_trans)), _CODES[x_gathered.dtype], _ptr(bias), out.data_ptr(),
         _ptr(ready_flags), _ptr(flag_counters), epoch, comm_turn, in_flags.data_ptr(), in_epoch,
-        spin_limit, _ptr(dev_err), _stream(dev))
+        spin_limit, _ptr(dev_err), ws, ws_bytes, _stream(dev))
     _check("mc2_ag_mm_local_inflags", st)
     return out
 

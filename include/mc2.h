@@ -14,7 +14,7 @@
  *
  * Conventions shared by every entry point:
  *   - All pointers are device pointers unless stated; the caller owns every
- *     buffer. The library allocates no device memory.
+ *     buffer (workspaces included). The library allocates no device memory.
  *   - Every call validates its arguments on the host first. On failure it
  *     returns a nonzero mc2_status and enqueues nothing.
  *   - On success the work is enqueued on `stream` and the call returns at once;
@@ -66,7 +66,8 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
                                 /* the counted rows exceed a buffer's rows     */
 #define MC2_DEVERR_INDEX 4u     /* an unpermute index outside the y buffer     */
 #define MC2_DEVERR_TIMEOUT 8u   /* an input ready flag did not arrive within
-                                   the spin limit                             */
+                                   the spin limit (or, never expected, a
+                                   K-split partner's partial within ~1 s)     */
 
 /*
  * mc2_mm_rs_local -- MatmulReduceScatter compute share [RS].
@@ -77,8 +78,8 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
  * and destination chunk c (c < world_size) is rows [c*m/W, (c+1)*m/W) of the
  * (m, n) result `out`. nsim == 1 computes this rank's own partial (the real
  * per-rank share); nsim == world_size sums the W stacked partials on one
- * device (the reduce-scatter arithmetic), accumulating all W*k products in one
- * fp32 (or int32) accumulator and rounding once.
+ * device (the reduce-scatter arithmetic), accumulating all W*k products in
+ * fp32 (or int32) and rounding once to the output dtype.
  *
  *   x1      (nsim, m, k) in_dtype             x2  (nsim, k, n), or (nsim, n, k)
  *                                                 when x2_trans != 0
@@ -118,13 +119,58 @@ typedef enum mc2_act { MC2_ACT_NONE = 0, MC2_ACT_SWIGLU = 1 } mc2_act;
  * memory; the last tile to finish segment g stores ready_flags[g] = epoch
  * with release ordering at system scope once every byte of segment g is
  * visible. epoch must be nonzero and should differ between calls. Both flag
- * pointers NULL disables flags. Results do not depend on comm_turn.
+ * pointers NULL disables flags.
+ *
+ * K split of the last round (stream-K for a thin tail) [RS "参数说明":
+ * comm_turn, the split granularity; the split here is of the work, not of
+ * the chunks]: with 256 x 256 tiles, a last dispatch round (one tile per CU)
+ * that is at most half full would leave CUs idle. With a workspace, each of
+ * its tiles runs as two K halves on two workgroups that exchange fp32 (int32)
+ * partials: the tile's value is then (sum over the first half of the K loop)
+ * + (sum over the second), one addition that gives the same bits whichever
+ * workgroup performs it. Without one, such a round runs as 128-row halves.
+ * (The split is switched off in this build while a fix of its partial
+ * stores awaits its device check: a workspace is accepted and ignored.)
+ *   workspace        NULL (no K split) or a 16-byte aligned buffer of
+ *                    workspace_bytes; its first 4096 bytes (control words)
+ *                    must be zero before the first call, and every call
+ *                    leaves them zero. mc2_split_workspace_size() bytes
+ *                    suffice for every call on the current device; a smaller
+ *                    one disables the split where it does not fit. Calls that
+ *                    overlap in time must not share a workspace.
+ * int8 results are exact whatever the schedule. Float results do not depend
+ * on comm_turn except through which tiles fall into a split last round:
+ * there the two fp32 halves add with one extra fp32 rounding. A call with the
+ * same arguments always gives the same bits.
  */
 int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
                     int world_size, int rank, int nsim, int x2_trans, int in_dtype,
                     const void* bias, const float* x1_scale, const float* x2_scale,
                     int out_dtype, void* out, uint32_t* ready_flags,
-                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, hipStream_t stream);
+                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of a K-split workspace that covers every call of mc2_mm_rs_local,
+ * mc2_ag_mm_local and mc2_ag_mm_local_inflags on the current device: 4096
+ * bytes of control words plus two 128 KiB partial slots per pair of
+ * workgroups (half the compute units). 32 MiB + 4 KiB on 256 CUs.
+ */
+size_t mc2_split_workspace_size(void);
+
+/*
+ * Policy of the K split, process-wide (tuning and tests):
+ *   MC2_SPLIT_PAIR   (default) the first K half to finish waits for its
+ *                    partner when the partner is running, and each finalizes
+ *                    one 128-row half of the tile (128 KiB moved each way);
+ *   MC2_SPLIT_ALONE  the first K half to start never waits: it hands its
+ *                    whole 256 KiB partial over and the other finalizes the
+ *                    whole tile.
+ * Both give bitwise the same results. Returns MC2_ERR_SHAPE for another value.
+ */
+#define MC2_SPLIT_PAIR 0
+#define MC2_SPLIT_ALONE 1
+int mc2_set_split_policy(int policy);
 
 /*
  * mc2_ag_mm_local -- AllGatherMatmul compute share [AG]: out = allgather(x1) @ x2
@@ -135,14 +181,16 @@ int mc2_mm_rs_local(const void* x1, const void* x2, int64_t m, int64_t k, int64_
  *   (MC2_F16 or MC2_BF16). out (W*m_c, n) in_dtype.
  *
  * Chunks are computed in the order (rank + i) mod W, starting with the chunk
- * this rank owns. comm_turn pieces and ready flags as for mc2_mm_rs_local
- * (W * max(comm_turn, 1) segments, 0 <= comm_turn <= m_c). Constraints:
- * k >= 1, k % 8 == 0, n % 8 == 0, m_c >= 1, world_size in {1, 2, 4, 8, 16, 32}.
+ * this rank owns. comm_turn pieces, ready flags and the K-split workspace
+ * as for mc2_mm_rs_local (W * max(comm_turn, 1) segments,
+ * 0 <= comm_turn <= m_c). Constraints: k >= 1, k % 8 == 0, n % 8 == 0,
+ * m_c >= 1, world_size in {1, 2, 4, 8, 16, 32}.
  */
 int mc2_ag_mm_local(const void* x_gathered, const void* x2, int64_t m_c, int64_t k,
                     int64_t n, int world_size, int rank, int x2_trans, int in_dtype,
                     const void* bias, void* out, uint32_t* ready_flags,
-                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, hipStream_t stream);
+                    uint32_t* flag_counters, uint32_t epoch, int comm_turn, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * mc2_ag_mm_local_inflags -- mc2_ag_mm_local whose tiles wait for their input
@@ -176,7 +224,7 @@ int mc2_ag_mm_local_inflags(const void* x_gathered, const void* x2, int64_t m_c,
                             uint32_t* flag_counters, uint32_t epoch, int comm_turn,
                             const uint32_t* in_flags,
                             uint32_t in_epoch, uint32_t spin_limit, int32_t* dev_err,
-                            hipStream_t stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * MatmulAllReduce local share ["NPU Training Operators - MC2", "底层 API 对照":

@@ -31,7 +31,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 18, names
+    assert len(names) == 20, names
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES, n
@@ -53,7 +53,7 @@ def rs(lib, **over):
     return lib.mc2_mm_rs_local(a["x1"], a["x2"], a["m"], a["k"], a["n"], a["W"], a["rank"],
                                a["nsim"], a["trans"], a["dt"], a["bias"], a["s1"], a["s2"],
                                a["odt"], a["out"], a["flags"], a["cnt"], a["epoch"], a["turn"],
-                               None)
+                               a.get("ws"), a.get("ws_bytes", 0), None)
 
 
 @pytest.mark.parametrize("over,code", [
@@ -81,6 +81,7 @@ def rs(lib, **over):
     (dict(flags=FAKE, cnt=FAKE, epoch=0), ERR_SHAPE),
     (dict(turn=-1), ERR_SHAPE),           # comm_turn >= 0
     (dict(turn=65), ERR_SHAPE),           # at most m / W pieces (64 rows per chunk)
+    (dict(ws=FAKE + 8, ws_bytes=1 << 20), ERR_ALIGN),  # the K-split workspace
 ])
 def test_mm_rs_rejects(lib, over, code):
     assert rs(lib, **over) == code
@@ -88,14 +89,31 @@ def test_mm_rs_rejects(lib, over, code):
 
 def test_ag_mm_rejects(lib):
     f = lib.mc2_ag_mm_local
-    tail = (None, None, 0, 0, None)
+    tail = (None, None, 0, 0, None, 0, None)
     assert f(None, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_NULL
     assert f(FAKE, FAKE, 16, 512, 64, 8, 8, 0, BF16, None, FAKE, *tail) == ERR_SHAPE
     assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, I8, None, FAKE, *tail) == ERR_DTYPE
     assert f(FAKE, FAKE, 16, 500, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_ALIGN
     assert f(FAKE, FAKE, 0, 512, 64, 8, 0, 0, BF16, None, FAKE, *tail) == ERR_SHAPE
-    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, 17, None) == ERR_SHAPE
-    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, -1, None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, 17, None, 0,
+             None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, -1, None, 0,
+             None) == ERR_SHAPE
+    assert f(FAKE, FAKE, 16, 512, 64, 8, 0, 0, BF16, None, FAKE, None, None, 0, 0, FAKE + 4,
+             1 << 20, None) == ERR_ALIGN
+
+
+def test_split_workspace_size_and_policy(lib):
+    """The K-split workspace: 4096 bytes of control words, then two 128 KiB
+    partial slots per pair of workgroups (half the CUs; 256 where no GPU is
+    visible). The policy setter takes the two documented values only."""
+    ws = lib.mc2_split_workspace_size()
+    assert ws > 4096 and (ws - 4096) % (2 * 128 * 1024) == 0
+    assert ws - 4096 <= 256 * 2 * 128 * 1024
+    assert lib.mc2_set_split_policy(2) == ERR_SHAPE
+    assert lib.mc2_set_split_policy(-1) == ERR_SHAPE
+    assert lib.mc2_set_split_policy(1) == MC2_OK
+    assert lib.mc2_set_split_policy(0) == MC2_OK
 
 
 def test_moe_entry_points_reject(lib):
@@ -139,12 +157,14 @@ def test_noalloc_permute_rejects_sizes_beyond_its_scratch(lib):
 def test_ag_mm_inflags_validates(lib):
     f = lib.mc2_ag_mm_local_inflags
     base = (FAKE, FAKE, 100, 512, 264, 8, 0, 0, BF16, None, FAKE, None, None, 0, 0)
-    assert f(*base, None, 1, 100, None, None) == ERR_NULL      # in_flags required
-    assert f(*base, FAKE, 0, 100, None, None) == ERR_SHAPE     # in_epoch != 0
-    assert f(*base, FAKE, 1, 0, None, None) == ERR_SHAPE       # spin_limit >= 1
-    assert f(None, *base[1:], FAKE, 1, 100, None, None) == ERR_NULL
-    assert f(*base[:8], I8, *base[9:], FAKE, 1, 100, None, None) == ERR_DTYPE
-    assert f(*base[:14], 101, FAKE, 1, 100, None, None) == ERR_SHAPE   # comm_turn <= m_c
+    nows = (None, 0, None)
+    assert f(*base, None, 1, 100, None, *nows) == ERR_NULL      # in_flags required
+    assert f(*base, FAKE, 0, 100, None, *nows) == ERR_SHAPE     # in_epoch != 0
+    assert f(*base, FAKE, 1, 0, None, *nows) == ERR_SHAPE       # spin_limit >= 1
+    assert f(None, *base[1:], FAKE, 1, 100, None, *nows) == ERR_NULL
+    assert f(*base[:8], I8, *base[9:], FAKE, 1, 100, None, *nows) == ERR_DTYPE
+    assert f(*base[:14], 101, FAKE, 1, 100, None, *nows) == ERR_SHAPE   # comm_turn <= m_c
+    assert f(*base, FAKE, 1, 100, None, FAKE + 8, 1 << 20, None) == ERR_ALIGN
 
 
 def test_mm_ar_validates(lib):
@@ -207,7 +227,7 @@ def test_header_is_plain_c_and_links_from_c(tmp_path):
         'int main(void) {\n'
         '  printf("%s|%s|%d\\n", mc2_version(), mc2_status_string(MC2_ERR_SHAPE),\n'
         '         mc2_mm_rs_local(0, 0, 1, 1, 1, 1, 0, 1, 0, MC2_BF16, 0, 0, 0, MC2_BF16, 0, 0, 0,\n'
-        '                         0, 0, 0));\n'
+        '                         0, 0, 0, 0, 0));\n'
         '  return 0;\n}\n')
     libdir = os.path.dirname(_lib.LIB_PATH)
     exe = tmp_path / "use"
