@@ -80,6 +80,23 @@ struct Tile {
   static constexpr int kStages = 2;
 };
 
+// Where accumulator element i of fragment (fm, fn) of a lane sits in the
+// wave's sub-tile (add wrow0 / wcol0). The eight-wave loop keeps the MFMA's
+// own layout: a lane holds one column, four consecutive rows. The four-wave
+// loop passes the two operands the other way round (it computes each 16 x 16
+// block transposed), so a lane holds four consecutive columns of one row and
+// its epilogue can store 8 or 16 contiguous bytes straight from registers.
+template <class TS>
+struct AccLayout {
+  static constexpr bool kRowRuns = TS::NW == 4;
+  static __device__ __forceinline__ int row(int fm, int lane, int i) {
+    return kRowRuns ? fm * 16 + (lane & 15) : fm * 16 + 4 * (lane >> 4) + i;
+  }
+  static __device__ __forceinline__ int col(int fn, int lane, int i) {
+    return kRowRuns ? fn * 16 + 4 * (lane >> 4) + i : fn * 16 + (lane & 15);
+  }
+};
+
 template <Elem E> struct Mma;
 template <> struct Mma<Elem::BF16> {
   using acc_t = f32x4_t;

@@ -14,6 +14,11 @@
 // two stages live in a two-buffer ring, and a load instruction moves 8 rows
 // of 128 bytes.
 //
+// Each MFMA takes the B fragment as its first operand and the A fragment as
+// its second (both are "row j of a 16-row slice, 8 or 16 K values" per lane),
+// so it computes the 16 x 16 block transposed: a lane ends with four
+// consecutive columns of one output row (AccLayout).
+//
 // One wave issues everything in one stream, so the stage is a fixed
 // interleave of its 2 x 64 MFMAs (16 cycles each) with the memory
 // instructions, one memory instruction after an MFMA at most, so that a load
@@ -329,11 +334,11 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       if constexpr (q == MM) tie(a1, b1);
       if constexpr (q < MM) {
         if constexpr (FIRST)
-          MmaA<E>::init(acc[fm][fn], a0[fm], b0.get(fn));
+          MmaA<E>::init(acc[fm][fn], b0.get(fn), a0[fm]);
         else
-          MmaA<E>::acc(acc[fm][fn], a0[fm], b0.get(fn));
+          MmaA<E>::acc(acc[fm][fn], b0.get(fn), a0[fm]);
       } else {
-        MmaA<E>::acc(acc[fm][fn], a1[fm], b1.get(fn));
+        MmaA<E>::acc(acc[fm][fn], b1.get(fn), a1[fm]);
       }
       if constexpr (q < NR) {
         read_op(std::integral_constant<int, q>{}, Pc, I1{}, a1, b1);

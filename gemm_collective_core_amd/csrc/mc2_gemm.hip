@@ -133,7 +133,36 @@ __device__ __forceinline__ void store_tile(const ChunkedArgs& p, lds_t* smem,
   const bool mine = (halves >> rh) & 1;  // uniform over the wave
   const int lo = halves == 2 ? TS::BM / 2 : 0;
   const int nr = halves == 3 ? TS::BM : TS::BM / 2;
-  if constexpr (OS == 2) {
+  if constexpr (TS::NW == 4 && OS == 2) {
+    // runs of four columns per lane: one 8-byte LDS write per run, then
+    // 16-byte coalesced stores of whole rows (stores of the 8-byte runs
+    // straight from the registers, 16 rows x 32 bytes per instruction, were
+    // measured far slower: partial lines reach memory)
+    constexpr int pitch = TS::BN * OS + 16;
+    if (mine)
+      epilogue_quads<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                               [&](int rr, int cc, const auto& v) {
+                                 *reinterpret_cast<MC2_LDS u32x2_t*>(smem + rr * pitch + cc * OS) =
+                                     pack4<O>(v);
+                               });
+    __syncthreads();
+    store_staged<TS::NT>(smem + lo * pitch, pitch, TS::BN * OS, nr, p.out + (row0 + lo) * p.ldo,
+                         p.ldo, row_end - (row0 + lo), col0 * OS, p.n * OS, p.store_wt != 0);
+  } else if constexpr (TS::NW == 4) {
+    // 32-bit test outputs: runs of four columns, 16-byte stores straight from
+    // the registers. n is a multiple of 8, so a run is either wholly inside
+    // the output or wholly past its last column.
+    char* base = p.out + row0 * p.ldo + col0 * OS;
+    const int64_t nrows = row_end - row0, ncols = p.n - col0;
+    const bool wt = p.store_wt != 0;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base);
+    if (mine)
+      epilogue_quads<E, TS, O>(acc, row0, row_end - 1, col0, p.n, p.bias, p.bias_mul, p.s1, p.s2,
+                               [&](int rr, int cc, const auto& v) {
+                                 if (rr < nrows && cc < ncols)
+                                   store4<O>(base, r, rr * p.ldo + cc * OS, v, wt);
+                               });
+  } else if constexpr (OS == 2) {
     // 16-bit outputs: stage the rows in LDS, then 16-byte coalesced stores.
     constexpr int pitch = TS::BN * OS + 16;
     if (mine)
@@ -211,6 +240,13 @@ __device__ __forceinline__ void count_tile(const ChunkedArgs& p, int g, int seg_
 // waits for its stores to complete before the control word is set. So no
 // L2 write-back or invalidate is taken, which would cost the other tiles on
 // the XCD their cached operands.
+
+// The K split is switched off: its first device runs faulted on the partial
+// stores (a scalar base address read too soon after v_readfirstlane wrote
+// it; fixed below with the wait states), and the fix has not yet run on the
+// device. Until it has, a workspace is accepted and ignored, a thin last
+// round runs as 128-row halves, and the split code is compiled out.
+constexpr bool kSplitEnabled = false;
 
 constexpr int64_t kPartBytes = 128 * 256 * 4;  // a row half of a 256 x 256 tile, 32-bit
 constexpr int64_t kSplitCtlBytes = 4096;       // control words of up to 256 pairs
@@ -408,7 +444,7 @@ __global__ __launch_bounds__(TS::NT, 1) void chunked_gemm_kernel(ChunkedArgs p) 
   if constexpr (TS::BM == 256) {
     if (u >= p.n_full) {
       const int v = u - p.n_full;
-      if (!p.sk_part) {
+      if (!kSplitEnabled || !p.sk_part) {
         using TH = Tile<128, TS::BN, TS::WM, TS::WN>;
         chunked_tile<E, BT, TH, O, KT>(p, smem, p.n_full + (v >> 1), v & 1, 1u);
         return;
@@ -479,12 +515,6 @@ static int64_t chunk_tiles(int64_t sq, int sr, int sub, int bm, int64_t tn) {
 // transfers per workgroup cost about as much as 4 stages.
 constexpr int kSplitMinStages = 16;
 
-// The K split is switched off: its first device runs faulted on the partial
-// stores (a scalar base address read too soon after v_readfirstlane wrote
-// it; fixed above with the wait states), and the fix has not yet run on the
-// device. Until it has, a workspace is accepted and ignored, and a thin last
-// round runs as 128-row halves.
-constexpr bool kSplitEnabled = false;
 
 // Tile shape for a problem: 0 = 256 x 256, 1 = 128 x 256. Costs are counted
 // in eighths of a round of 256 x 256 tiles: a thin last round costs 5 when

@@ -12,26 +12,30 @@ namespace mc2 {
 
 // SwiGLU epilogue: tile column blocks alternate gate (even) and up (odd), so
 // the fragments fn = 2p and 2p + 1 of a lane hold gate and up of the same
-// output column. h = silu(g) * u, silu(g) = g / (1 + exp(-g)), stored as bf16.
+// output columns. h = silu(g) * u, silu(g) = g / (1 + exp(-g)), stored as
+// bf16. The four-wave accumulators hold runs of four output columns per lane:
+// one 8-byte LDS write per run (staged for whole-row stores).
 template <class TS>
 __device__ __forceinline__ void stage_swiglu(lds_t* smem, int pitch,
                                              const f32x4_t (&acc)[TS::FM][TS::FN]) {
+  static_assert(AccLayout<TS>::kRowRuns, "runs of four columns");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
 #pragma unroll
   for (int p = 0; p < TS::FN / 2; ++p) {
-    const int lcol = wcol0 / 2 + p * 16 + (lane & 15);
+    const int lcol = wcol0 / 2 + p * 16 + 4 * (lane >> 4);
 #pragma unroll
     for (int fm = 0; fm < TS::FM; ++fm) {
+      const int lrow = wrow0 + fm * 16 + (lane & 15);
+      float h[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int lrow = wrow0 + fm * 16 + 4 * (lane >> 4) + i;
         const float g = acc[fm][2 * p][i];
         const float u = acc[fm][2 * p + 1][i];
-        const float h = g / (1.0f + __expf(-g)) * u;
-        *reinterpret_cast<MC2_LDS uint16_t*>(smem + lrow * pitch + lcol * 2) = f32_to_bf16_bits(h);
+        h[i] = g / (1.0f + __expf(-g)) * u;
       }
+      *reinterpret_cast<MC2_LDS u32x2_t*>(smem + lrow * pitch + lcol * 2) = pack4<Out::BF16>(h);
     }
   }
 }
@@ -123,16 +127,16 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (
   for (int half = 0; half < 2; ++half) {
     __syncthreads();
     if (wrow0 == half * HR) {
+      // runs of four columns per lane (AccLayout of the four-wave tiles)
+      static_assert(AccLayout<TS>::kRowRuns, "runs of four columns");
 #pragma unroll
       for (int fn = 0; fn < TS::FN; ++fn) {
-        const int lcol = wcol0 + fn * 16 + (lane & 15);
+        const int lcol = wcol0 + fn * 16 + 4 * (lane >> 4);
 #pragma unroll
-        for (int fm = 0; fm < TS::FM; ++fm)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int lrow = fm * 16 + 4 * (lane >> 4) + i;
-            *reinterpret_cast<MC2_LDS float*>(smem + lrow * pitch + lcol * 4) = acc[fm][fn][i];
-          }
+        for (int fm = 0; fm < TS::FM; ++fm) {
+          const int lrow = fm * 16 + (lane & 15);
+          *reinterpret_cast<MC2_LDS f32x4_t*>(smem + lrow * pitch + lcol * 4) = acc[fm][fn];
+        }
       }
     }
     __syncthreads();
@@ -301,9 +305,11 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
     if constexpr (GLU)
       stage_swiglu<TSX>(smem, pitch, acc);
     else
-      epilogue_linear<Elem::BF16, TSX, Out::BF16>(
+      epilogue_quads<Elem::BF16, TSX, Out::BF16>(
           acc, orow0, 0, ocol0, p.n_out, nullptr, 0.f, nullptr, nullptr,
-          [&](int r, int c, float v) { put_out<Out::BF16>(smem + r * pitch + c * 2, v); });
+          [&](int rr, int cc, const auto& v) {
+            *reinterpret_cast<MC2_LDS u32x2_t*>(smem + rr * pitch + cc * 2) = pack4<Out::BF16>(v);
+          });
     __syncthreads();
     store_staged<TSX::NT>(smem, pitch, OUTC * 2, TSX::BM, p.out + orow0 * p.ldo, p.ldo, arow_end - arow0,
                  ocol0 * 2, p.n_out * 2);
