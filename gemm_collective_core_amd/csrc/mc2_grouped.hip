@@ -257,6 +257,14 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
     int g;
     int64_t tm, tn;
   };
+  // Inside a group, tiles go in bands of `band` row blocks: a band's tiles
+  // run row block fastest, column tile by column tile, and the bands follow
+  // each other. With band x tiles_n close to the 32 tiles an XCD takes per
+  // round, the tiles that share one L2 cover a few row blocks and all column
+  // tiles (fc2: 4 x 8), instead of 32 row blocks of one column tile, so the
+  // K slabs of each A row block and B column block are fetched into that L2
+  // once for all the tiles that use them.
+  const int64_t band = tiles_n < 32 ? 32 / tiles_n : 1;
   auto place = [&](int64_t t) {
     int g = 0;
     while (g + 1 < El && s_tstart[g + 1] <= t) ++g;
@@ -264,8 +272,11 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
     const int64_t cnt = uni(s_gstart[g + 1]) - uni(s_gstart[g]);
     const int64_t tiles_m = (cnt + TS::BM - 1) / TS::BM;
     const int64_t lt = t - uni(s_tstart[g]);
-    // 64-bit division runs on the vector ALU: its results are made uniform again
-    return Place{g, uni(lt % tiles_m), uni(lt / tiles_m)};
+    // 64-bit divisions run on the vector ALU: their results are made uniform again
+    const int64_t b = uni(lt / (band * tiles_n));
+    const int64_t in_b = lt - b * band * tiles_n;
+    const int64_t rows_b = tiles_m - b * band < band ? tiles_m - b * band : band;
+    return Place{g, uni(b * band + in_b % rows_b), uni(in_b / rows_b)};
   };
   // One output tile of TSX::BM rows (TS, or its 128-row half) from row r0 of
   // group g, column tile tn.
