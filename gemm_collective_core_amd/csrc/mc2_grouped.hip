@@ -575,8 +575,10 @@ struct WgradArgs {
 // acquire, as the ready flags) sums the partials in slice order, so the result
 // does not depend on timing. An empty group gets zeros. The grid may have more
 // workgroups than units (the host knows only a bound); the rest exit.
-template <class TS>
-__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
+// KT: the K extent of a unit may end inside a stage (four-wave tiles; the
+// eight-wave loop always checks).
+template <class TS, bool KT>
+__global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   constexpr int kSmem = TS::kStages * TS::kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   __shared__ GroupTable t;
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
   const int El = p.local_experts;
   const int per_group = p.tiles_m * p.tiles_n;
-  for (int e = threadIdx.x; e < El; e += kThreads) {
+  for (int e = threadIdx.x; e < El; e += TS::NT) {
     const int32_t c = t.cnt[e];
     int rank = 0;
     for (int f = 0; f < El; ++f) rank += t.cnt[f] > c || (t.cnt[f] == c && f < e);
@@ -633,7 +635,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
   if (cnt == 0) {
-    for (int i = threadIdx.x; i < TS::BM * TS::BN; i += kThreads) {
+    for (int i = threadIdx.x; i < TS::BM * TS::BN; i += TS::NT) {
       const int r = i / TS::BN, c = i - r * TS::BN;
       if (r < nrows && c < ncols) dst[(row0 + r) * p.N + col0 + c] = 0.0f;
     }
@@ -646,15 +648,30 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   f32x4_t acc[TS::FM][TS::FN];
   BDesc bd{p.Q + (base + gstart + k0) * p.ldq, p.ldq, p.N};
   PlainCols cm{col0, p.N - 8};
-  mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
-                                  col0, cm, ks, acc);
+  if constexpr (TS::NW == 4)
+    mainloop_w4<Elem::BF16, false, TS, KT>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1,
+                                           bd, col0, cm, ks, acc);
+  else
+    mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
+                                    col0, cm, ks, acc);
   if (nslices == 1) {
     char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
-    epilogue_linear<Elem::BF16, TS, Out::F32>(
-        acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr, [&](int r, int c, float v) {
-          if (r < nrows && c < ncols)
-            __builtin_nontemporal_store(v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
-        });
+    if constexpr (TS::NW == 4) {
+      // runs of four columns (N is a multiple of 8): one 16-byte store each
+      epilogue_quads<Elem::BF16, TS, Out::F32>(
+          acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr,
+          [&](int r, int c, const auto& v) {
+            if (r < nrows && c < ncols)
+              __builtin_nontemporal_store(pack4<Out::F32>(v),
+                                          reinterpret_cast<u32x4_t*>(base_out + (r * p.N + c) * 4));
+          });
+    } else {
+      epilogue_linear<Elem::BF16, TS, Out::F32>(
+          acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr, [&](int r, int c, float v) {
+            if (r < nrows && c < ncols)
+              __builtin_nontemporal_store(v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
+          });
+    }
     return;
   }
   // split group: this slice's partial tile (dense BM x BN) into its slot
@@ -662,10 +679,17 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   float* part0 = p.partials + (uni(s_slot[g]) * per_group + lt) * kTileElems;
   const int64_t slice_stride = per_group * kTileElems;
   char* mine = reinterpret_cast<char*>(part0 + s * slice_stride);
-  epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                            nullptr, [&](int r, int c, float v) {
-                                              put_out_global<Out::F32>(mine + (r * TS::BN + c) * 4, v);
-                                            });
+  if constexpr (TS::NW == 4)
+    epilogue_quads<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
+                                             nullptr, [&](int r, int c, const auto& v) {
+                                               *reinterpret_cast<u32x4_t*>(mine + (r * TS::BN + c) * 4) =
+                                                   pack4<Out::F32>(v);
+                                             });
+  else
+    epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
+                                              nullptr, [&](int r, int c, float v) {
+                                                put_out_global<Out::F32>(mine + (r * TS::BN + c) * 4, v);
+                                              });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t* ctr = p.counters + static_cast<int64_t>(g) * per_group + lt;
@@ -677,7 +701,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(WgradArgs p) {
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  for (int i = threadIdx.x; i < TS::BM * TS::BN / 4; i += kThreads) {
+  for (int i = threadIdx.x; i < TS::BM * TS::BN / 4; i += TS::NT) {
     const int r = i / (TS::BN / 4), c = (i - r * (TS::BN / 4)) * 4;
     if (r >= nrows || c >= ncols) continue;
     float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -901,8 +925,8 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   // at most rows / L + E_l slices in all
   const int64_t units = (p_cap / kSliceRows + local_experts) * per_group;
   if (units > 0x3fffffff) return MC2_ERR_SHAPE;
-  hipLaunchKernelGGL((wgrad_kernel<TileL>), dim3(static_cast<unsigned>(units)), dim3(kThreads), 0,
-                     stream, w);
+  hipLaunchKernelGGL((wgrad_kernel<TileW, true>), dim3(static_cast<unsigned>(units)),
+                     dim3(TileW::NT), 0, stream, w);
   return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 
