@@ -552,7 +552,8 @@ struct WgradArgs {
   float* out;         // (E_l, M, N) fp32
   int64_t M, N;
   int tiles_m, tiles_n;
-  int round;
+  int q;              // units per XCD per slice: ceil(tiles_m * tiles_n / 8)
+  int bm, bn;         // an XCD's q tiles of a slice as a bm x bn block (bm = 0: a run of q)
   uint32_t* counters; // E_l * tiles_m * tiles_n, zero on entry (left zero)
   float* partials;    // max_slots slices' partial tiles of split groups
   int64_t max_slots;
@@ -565,10 +566,16 @@ struct WgradArgs {
 // dW[g] = P_g^T @ Q_g (M x N per local group g). Work unit = (group g, K
 // slice s, tile): a 256 x 256 tile over rows [s*L, min((s+1)*L, count g)) of
 // the group, L = kSliceRows; A is the group's column range of the transposed
-// workspace, B the group's rows of Q. Units are numbered group by group, the
+// workspace, B the group's rows of Q. Slices are numbered group by group, the
 // groups with most rows first (so the longest units are dispatched first and
-// the short ones fill the end of the launch), slice by slice, tile fastest. A
-// group of one slice stores its tile (non-temporal: the result is not read
+// the short ones fill the end of the launch). Workgroup b runs on XCD b % 8,
+// and each XCD takes q tiles of every slice, slice after slice: the XCDs get
+// the same unit lengths, so none of them is left with the long units while
+// the others idle (numbering units in order and giving each XCD a run of 32
+// put the longest of every round on the same XCD). An XCD's q tiles of a
+// slice form a bm x bn block where the tile grid splits into 8 such blocks,
+// so that they share A and B slabs in that XCD's L2; else a run of q tiles in
+// row-fastest order. A group of one slice stores its tile (non-temporal: the result is not read
 // again here; the same hint on the partials below, which are read back, was
 // slower); for a split group every slice stores its partial tile in its slot,
 // and the last slice to finish a tile (counted with an agent-scope release /
@@ -582,7 +589,7 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   constexpr int kSmem = TS::kStages * TS::kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   __shared__ GroupTable t;
-  __shared__ int64_t s_ustart[kMaxLocalExperts + 1];  // by position in the order
+  __shared__ int64_t s_sstart[kMaxLocalExperts + 1];  // first slice, by position in the order
   __shared__ int64_t s_slot[kMaxLocalExperts + 1];    // by group
   __shared__ int s_order[kMaxLocalExperts];           // position -> group
   __shared__ int s_last;
@@ -598,16 +605,16 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    int64_t u = 0, slot = 0;
+    int64_t sl = 0, slot = 0;
     for (int q = 0; q < El; ++q) {
       const int e = s_order[q];
       const int64_t ns = t.cnt[e] > kSliceRows ? (t.cnt[e] + kSliceRows - 1) / kSliceRows : 1;
-      s_ustart[q] = u;
+      s_sstart[q] = sl;
       s_slot[e] = slot;
-      u += ns * per_group;
+      sl += ns;
       slot += ns > 1 ? ns : 0;
     }
-    s_ustart[El] = u;
+    s_sstart[El] = sl;
     s_slot[El] = slot;
   }
   __syncthreads();
@@ -616,21 +623,33 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
     if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
     return;
   }
-  const int64_t u = xcd_tile(blockIdx.x, p.round, gridDim.x);
-  if (u >= uni(s_ustart[El])) return;
+  const int x = static_cast<int>(blockIdx.x & 7);
+  const int64_t j = blockIdx.x >> 3;
+  // 64-bit division runs on the vector ALU: its results are made uniform again
+  const int64_t sig = uni(j / p.q);
+  const int i = uni(static_cast<int>(j - sig * p.q));
+  if (sig >= uni(s_sstart[El])) return;
+  int tm, tn;
+  if (p.bm) {
+    const int xm = p.tiles_m / p.bm;
+    tm = uni((x % xm) * p.bm + i % p.bm);
+    tn = uni((x / xm) * p.bn + i / p.bm);
+  } else {
+    const int l = x * p.q + i;
+    if (l >= per_group) return;
+    tm = uni(l % p.tiles_m);
+    tn = uni(l / p.tiles_m);
+  }
+  const int lt = tm + tn * p.tiles_m;
   int q = 0;
-  while (q + 1 < El && s_ustart[q + 1] <= u) ++q;
+  while (q + 1 < El && s_sstart[q + 1] <= sig) ++q;
   q = uni(q);
   const int g = uni(s_order[q]);
-  const int64_t lu = u - uni(s_ustart[q]);
-  // 64-bit division runs on the vector ALU: its results are made uniform again
-  const int s = uni(static_cast<int>(lu / per_group));
-  const int lt = uni(static_cast<int>(lu - static_cast<int64_t>(s) * per_group));
-  const int tm = uni(lt % p.tiles_m), tn = uni(lt / p.tiles_m);
+  const int s = uni(static_cast<int>(sig - uni(s_sstart[q])));
   const int64_t row0 = static_cast<int64_t>(tm) * TS::BM;
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
   const int64_t cnt = uni(static_cast<int64_t>(t.cnt[g]));
-  const int64_t nslices = (uni(s_ustart[q + 1]) - uni(s_ustart[q])) / per_group;
+  const int64_t nslices = uni(s_sstart[q + 1]) - uni(s_sstart[q]);
   const int64_t gstart = uni(t.gstart[g]), pstart = uni(t.pstart[g]);
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
@@ -913,7 +932,15 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   w.N = N;
   w.tiles_m = static_cast<int>(L.tiles_m);
   w.tiles_n = static_cast<int>(L.tiles_n);
-  w.round = static_cast<int>(num_cus() / 8 * 8);
+  // q tiles of each slice per XCD; the block shape with the fewest A and B
+  // slabs (bm + bn) among those that cut the tile grid into 8 blocks
+  w.q = static_cast<int>((per_group + 7) / 8);
+  for (int a = 1; a <= w.q; ++a) {
+    const int b = w.q / a;
+    if (a * b != w.q || L.tiles_m % a || L.tiles_n % b || (L.tiles_m / a) * (L.tiles_n / b) != 8)
+      continue;
+    if (!w.bm || a + b < w.bm + w.bn) w.bm = a, w.bn = b;
+  }
   w.counters = t.zero;
   w.partials = reinterpret_cast<float*>(ws + L.off_part);
   w.max_slots = L.max_slots;
@@ -922,8 +949,8 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   w.ep_rank = ep_rank;
   w.local_experts = local_experts;
   w.dev_err = dev_err;
-  // at most rows / L + E_l slices in all
-  const int64_t units = (p_cap / kSliceRows + local_experts) * per_group;
+  // at most rows / L + E_l slices in all, q units of each per XCD
+  const int64_t units = (p_cap / kSliceRows + local_experts) * 8 * w.q;
   if (units > 0x3fffffff) return MC2_ERR_SHAPE;
   hipLaunchKernelGGL((wgrad_kernel<TileW, true>), dim3(static_cast<unsigned>(units)),
                      dim3(TileW::NT), 0, stream, w);
