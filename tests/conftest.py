@@ -33,3 +33,29 @@ def load_golden(name):
 @pytest.fixture
 def golden():
     return load_golden
+
+
+def device_asm(src, out, extra_inc=()):
+    """gfx950 assembly of one HIP source, compiled with the library's flags."""
+    import subprocess
+    from gemm_collective_core_amd import build
+    flags = [f for f in build.HIPCC_FLAGS if f != "-shared"]
+    cmd = [build.hipcc(), *flags, "-I", os.path.join(build.ROOT, "include"),
+           *[f"-I{d}" for d in extra_inc], "--cuda-device-only", "-S", src, "-o", out]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    with open(out, encoding="utf-8") as f:
+        return f.read()
+
+
+@pytest.fixture(scope="session")
+def library_asm(tmp_path_factory):
+    """{source path: assembly} of every library source, compiled once for the
+    static checks of the compiled kernels."""
+    from concurrent.futures import ThreadPoolExecutor
+    from gemm_collective_core_amd import build
+    d = tmp_path_factory.mktemp("asm")
+    srcs = [os.path.join(build.CSRC, s) for s in build.SOURCES]
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        texts = list(ex.map(lambda s: device_asm(s, str(d / (os.path.basename(s) + ".s"))), srcs))
+    return dict(zip(srcs, texts))

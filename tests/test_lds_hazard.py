@@ -4,8 +4,6 @@ flags the pattern that once produced wrong results: the compiler copying one
 dword of an asm operand read straight after issuing it."""
 import os
 import shutil
-import subprocess
-from concurrent.futures import ThreadPoolExecutor
 
 import pytest
 
@@ -84,27 +82,12 @@ def test_read_carried_over_a_loop_back_edge():
     assert len(h) == 1 and "v20, v2" in h[0]
 
 
-def _device_asm(src: str, out: str):
-    from gemm_collective_core_amd import build
-    flags = [f for f in build.HIPCC_FLAGS if f != "-shared"]
-    cmd = [build.hipcc(), *flags, "-I", os.path.join(build.ROOT, "include"),
-           "--cuda-device-only", "-S", src, "-o", out]
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    assert res.returncode == 0, res.stderr[-2000:]
-    with open(out, encoding="utf-8") as f:
-        return f.read()
-
-
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="hipcc is needed to compile the kernels")
-def test_compiled_kernels_have_no_in_flight_lds_access(tmp_path):
+def test_compiled_kernels_have_no_in_flight_lds_access(library_asm):
     """Every kernel of the library, compiled for gfx950 as the build compiles
     it."""
-    from gemm_collective_core_amd import build
-    srcs = [os.path.join(build.CSRC, s) for s in build.SOURCES]
-    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
-        texts = list(ex.map(lambda s: _device_asm(s, str(tmp_path / (os.path.basename(s) + ".s"))),
-                            srcs))
+    srcs, texts = list(library_asm), list(library_asm.values())
     found = {}
     nfun = 0
     for src, text in zip(srcs, texts):
