@@ -94,6 +94,20 @@ template <> struct MmaA<Elem::I8> {
   }
 };
 
+// F operand fragments of a wave for one k-step: 16-byte reads of a
+// K-contiguous operand (KC), or two 8-byte transposing reads of a k-major one
+// whose halves form the MFMA operand after the wait (so no register copy can
+// read a half still in flight).
+template <bool KC, int F>
+struct FragOps {
+  u32x4_t q[KC ? F : 1];
+  u32x2_t h[KC ? 1 : F][2];
+  __device__ __forceinline__ u32x4_t get(int f) const {
+    if constexpr (KC) return q[f];
+    else return u32x4_t{h[f][0][0], h[f][0][1], h[f][1][0], h[f][1][1]};
+  }
+};
+
 // Load j of a stage is issued at slot a + 1 + (j * span) / nl; the load
 // issued at slot q, or -1.
 constexpr int load_slot_index(int q, int a, int span, int nl) {
@@ -105,13 +119,16 @@ constexpr int load_slot_index(int q, int a, int span, int nl) {
 // BT: B given as (n, k) (K-contiguous, like A); otherwise row-major (k, n),
 // kept k-major in LDS and read with the transposing LDS reads (16-bit only),
 // `colmap(c)` giving the global column of tile column c (a multiple of 8).
+// AK: A given row-major (k, m) as well (`A` at its k row 0, `lda` bytes per k
+// row, m = row0 .. row_last a multiple of 8 wide), kept and read the same way
+// as row-major B (with row-major B and 256-row tiles only).
 // KTAIL: the shard's K extent may end inside a stage, so every load checks
 // its lanes against the K values left (lanes past the end load zeros);
 // without it (K a multiple of the stage) the loads carry no per-lane check.
 //
 // LDS: A of stage 0, B of stage 0, B of stage 1, A of stage 1, so that the
 // two B buffers lie within one immediate offset of each other.
-template <Elem E, bool BT, class TS, bool KTAIL, class ColMap>
+template <Elem E, bool BT, class TS, bool KTAIL, bool AK = false, class ColMap>
 __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t lda, int64_t row0,
                                             int64_t row_last, const BDesc& B, int64_t col0,
                                             const ColMap& colmap, const KSpan& ks,
@@ -124,9 +141,11 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   constexpr int NB = TS::BN / 32;   // B loads per wave per stage
   constexpr int NL = NA + NB;
   constexpr int NBR = BT ? FN : 2 * FN;  // B operand reads per k-step (8 bytes each if !BT)
-  constexpr int NR = FM + NBR;      // operand reads per wave per k-step
+  constexpr int NAR = AK ? 2 * FM : FM;  // A operand reads per k-step (8 bytes each if AK)
+  constexpr int NR = NAR + NBR;     // operand reads per wave per k-step
   static_assert(TS::NW == 4 && TS::BN == 256, "four waves, 256-column tiles");
   static_assert(BT || ES == 2, "row-major B: 16-bit elements");
+  static_assert(!AK || (!BT && TS::BM == 256), "row-major A: with row-major B, 256-row tiles");
   static_assert(NL <= 63, "vmcnt range of the prologue");
   constexpr int MM = FM * FN;       // MFMA slots per k-step
   // Slots q = 0 .. 2 MM - 1 of a stage (k-step 1 from MM on), one MFMA each:
@@ -157,10 +176,23 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   // columns of the 32-byte pair the k-major swizzle puts there.
   uint32_t l_off[NL];
   int l_key[NL];
+  // row-major A: the 8 rows of a 16-byte piece, the last piece clamped to the matrix
+  auto rowmap = [&](int c) {
+    const int64_t r = row0 + c;
+    return r < row_last - 7 ? r : row_last - 7;
+  };
 #pragma unroll
   for (int j = 0; j < NL; ++j) {
     const bool isa = j < NA;
-    if (isa || BT) {
+    if (AK && isa) {
+      const int o = (NA * wave + j) * 1024 + 16 * lane;
+      const int kr = o / (TS::BM * 2);
+      const int pc = (o - kr * (TS::BM * 2)) >> 4;
+      // (the swizzle is defined for 256-wide k rows; only AK tiles get here)
+      const int ch = (kmaj_unpos16<(AK ? TS::BM : 256)>(pc >> 1, kr) << 1) | (pc & 1);
+      l_off[j] = static_cast<uint32_t>(kr * lda + rowmap(ch * 8) * 2);
+      l_key[j] = kr;
+    } else if (isa || BT) {
       const int r = 8 * ((isa ? NA : NB) * wave + (isa ? j : j - NA)) + (lane >> 3);
       const int c = (row_off(r, lane & 7) - r * kKBytes) >> 4;
       if (isa) {
@@ -182,12 +214,15 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       l_key[j] = kr;
     }
   }
-  const char* a_base = A + row0 * lda;
+  const char* a_base = AK ? A : A + row0 * lda;
   const char* b_base = BT ? B.base + col0 * B.ld : B.base;
-  // LDS regions: A of stage p at a_lds(p), B of stage p at b_lds(p)
-  constexpr int kA1 = TS::kABytes + 2 * TS::kBBytes;
+  // LDS regions: A of stage p at a_lds(p), B of stage p at b_lds(p); with
+  // row-major A both A buffers come first (the transposing reads address
+  // them from one register, as the B buffers)
+  constexpr int kA1 = AK ? TS::kABytes : TS::kABytes + 2 * TS::kBBytes;
+  constexpr int kB0 = AK ? 2 * TS::kABytes : TS::kABytes;
   auto a_lds = [](int p) { return p ? kA1 : 0; };
-  auto b_lds = [](int p) { return TS::kABytes + p * TS::kBBytes; };
+  auto b_lds = [](int p) { return kB0 + p * TS::kBBytes; };
 
   // Loads of stage it: the buffer resources are formed once per stage; a
   // stage past the last one gets resources of no records, so its loads (the
@@ -210,10 +245,11 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
     const int64_t kl = ks.k - kdone;
     s.kleft = static_cast<int>(kl < (1 << 30) ? kl : (1 << 30));
     s.st = smem + ((ld_it & 1) ? kA1 : 0);
-    s.stb = smem + TS::kABytes + (ld_it & 1) * TS::kBBytes;
+    s.stb = smem + kB0 + (ld_it & 1) * TS::kBBytes;
     const int nrec = ld_it < n ? 0x7ffffff0 : 0;
     s.ra = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(a_base + lw * ks.a_shard + kdone * ES), 0, nrec, kBufFlags);
+        const_cast<char*>(a_base + lw * ks.a_shard + (AK ? kdone * lda : kdone * ES)), 0, nrec,
+        kBufFlags);
     s.rb = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<char*>(b_base + lw * ks.b_shard + (BT ? kdone * ES : kdone * B.ld)), 0, nrec,
         kBufFlags);
@@ -257,30 +293,39 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   if constexpr (!BT) {
     const int j = lane & 15, g = lane >> 4;
     const int swz = (j >> 2) | ((g & 1) << 2);
-    const uint32_t base = s0 + TS::kABytes + (g * 8 + (j >> 2)) * (TS::BN * 2) + ((j & 3) << 3);
+    const uint32_t base = s0 + kB0 + (g * 8 + (j >> 2)) * (TS::BN * 2) + ((j & 3) << 3);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
       adT[fn] = base + ((((wcol0 >> 4) | (fn ^ swz))) << 5);
   }
+  // Row-major A: the same with the wave's rows (wrow0 / 16 in {0, 8}) and
+  // A's buffers.
+  uint32_t adTA[AK ? FM : 1];
+  if constexpr (AK) {
+    const int j = lane & 15, g = lane >> 4;
+    const int swz = (j >> 2) | ((g & 1) << 2);
+    const uint32_t base = s0 + (g * 8 + (j >> 2)) * (TS::BM * 2) + ((j & 3) << 3);
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+      adTA[fm] = base + ((((wrow0 >> 4) | (fm ^ swz))) << 5);
+  }
 
-  // A fragments: 16-byte reads; B fragments: 16-byte reads (B as (n, k)) or
-  // two 8-byte transposing reads whose halves form the MFMA operand after
-  // the wait (so no register copy can read a half still in flight).
-  struct BOps {
-    u32x4_t q[BT ? FN : 1];
-    u32x2_t h[BT ? 1 : FN][2];
-    __device__ __forceinline__ u32x4_t get(int fn) const {
-      if constexpr (BT) return q[fn];
-      else return u32x4_t{h[fn][0][0], h[fn][0][1], h[fn][1][0], h[fn][1][1]};
-    }
-  };
-  u32x4_t a0[FM], a1[FM];
+  using AOps = FragOps<!AK, FM>;
+  using BOps = FragOps<BT, FN>;
+  AOps a0, a1;
   BOps b0, b1;
   // operand read number i of k-step K2 from buffer P: B reads first, then A
-  auto read_op = [&](auto I, auto Pc, auto K2c, u32x4_t (&a)[FM], BOps& b) {
+  auto read_op = [&](auto I, auto Pc, auto K2c, AOps& a, BOps& b) {
     constexpr int i = decltype(I)::value, P = decltype(Pc)::value, K2 = decltype(K2c)::value;
-    if constexpr (i >= NBR) {
-      a[i - NBR] = lds_rd128_at<(i - NBR) * 16 * kKBytes>(adA[P][K2]);
+    if constexpr (i >= NBR && AK) {
+      constexpr int fm = (i - NBR) / 2, h = (i - NBR) % 2;
+      constexpr int off = P * TS::kABytes + (32 * K2 + 4 * h) * TS::BM * 2;
+      static_assert(off < 65536, "ds_read offset field");
+      const uint32_t addr = adTA[fm];
+      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                   : "=v"(a.h[fm][h]) : "v"(addr), "i"(off) : "memory");
+    } else if constexpr (i >= NBR) {
+      a.q[i - NBR] = lds_rd128_at<(i - NBR) * 16 * kKBytes>(adA[P][K2]);
     } else if constexpr (BT) {
       b.q[i] = lds_rd128_at<i * 16 * kKBytes>(adB[P][K2]);
     } else {
@@ -292,9 +337,17 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
                    : "=v"(b.h[fn][h]) : "v"(addr), "i"(off) : "memory");
     }
   };
-  auto tie = [&](u32x4_t (&a)[FM], BOps& b) {
+  auto tie = [&](AOps& a, BOps& b) {
+    if constexpr (AK) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a[i]));
+      for (int i = 0; i < FM; ++i) {
+        asm volatile("" : "+v"(a.h[i][0]));
+        asm volatile("" : "+v"(a.h[i][1]));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(a.q[i]));
+    }
     if constexpr (BT) {
 #pragma unroll
       for (int i = 0; i < FN; ++i) asm volatile("" : "+v"(b.q[i]));
@@ -334,11 +387,11 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       if constexpr (q == MM) tie(a1, b1);
       if constexpr (q < MM) {
         if constexpr (FIRST)
-          MmaA<E>::init(acc[fm][fn], b0.get(fn), a0[fm]);
+          MmaA<E>::init(acc[fm][fn], b0.get(fn), a0.get(fm));
         else
-          MmaA<E>::acc(acc[fm][fn], b0.get(fn), a0[fm]);
+          MmaA<E>::acc(acc[fm][fn], b0.get(fn), a0.get(fm));
       } else {
-        MmaA<E>::acc(acc[fm][fn], b1.get(fn), a1[fm]);
+        MmaA<E>::acc(acc[fm][fn], b1.get(fn), a1.get(fm));
       }
       if constexpr (q < NR) {
         read_op(std::integral_constant<int, q>{}, Pc, I1{}, a1, b1);

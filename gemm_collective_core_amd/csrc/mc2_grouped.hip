@@ -74,6 +74,8 @@ struct GroupedArgs {
   int ktiles;
   const char* gsave;      // SwiGLU backward: the fc1 pre-activation (rows, 2*inter) bf16
   int64_t ldg;            // bytes per gsave row
+  uint32_t* zero;         // n_zero words that workgroup 0 clears first (the backward's
+  int64_t n_zero;         // weight-gradient tile counters, used by the next launch), or null
 };
 
 // Epilogue of the grouped kernel.
@@ -198,6 +200,10 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
   const int tid = threadIdx.x;
   const int El = p.local_experts;
   const int first = p.ep_rank * El;
+  if constexpr (BT) {  // the input-gradient launches of the backward
+    if (p.zero && blockIdx.x == 0)
+      for (int64_t i = tid; i < p.n_zero; i += TS::NT) p.zero[i] = 0;
+  }
   constexpr int OUTC = GLU ? TS::BN / 2 : TS::BN;  // output columns per tile
   const int64_t tiles_n = (p.n_out + OUTC - 1) / OUTC;
 
@@ -348,18 +354,12 @@ __global__ __launch_bounds__(TS::NT, 1) void grouped_gemm_kernel(GroupedArgs p) 
 // ---------------------------------------------------------------- weight gradients
 
 // Group table of the local experts from the device-side counts, in shared
-// memory: row starts (gstart), starts of each group's columns in the
-// transposed workspace (pstart: group sizes rounded up to 64, so that every
-// 64-element K stage of a group is one aligned 128-byte line), and the
-// send-buffer row of local expert 0 (base). bad is set when the counts are
-// negative or recv_counts disagree with the send counts of this rank's
-// experts. The counts are read by many threads at once; one thread then sums
-// them in shared memory.
-constexpr int kGroupAlign = 64;
-
+// memory: row starts (gstart) and the send-buffer row of local expert 0
+// (base). bad is set when the counts are negative or recv_counts disagree
+// with the send counts of this rank's experts. The counts are read by many
+// threads at once; one thread then sums them in shared memory.
 struct GroupTable {
   int64_t gstart[kMaxLocalExperts + 1];
-  int64_t pstart[kMaxLocalExperts + 1];
   int32_t cnt[kMaxLocalExperts];
   int64_t base;
   int bad;
@@ -387,164 +387,23 @@ __device__ __forceinline__ void load_group_table(GroupTable& t, const int32_t* s
   }
   __syncthreads();
   if (tid == 0) {
-    int64_t g = 0, q = 0;
+    int64_t g = 0;
     for (int e = 0; e < El; ++e) {
-      const int64_t c = t.cnt[e];
       t.gstart[e] = g;
-      t.pstart[e] = q;
-      g += c;
-      q += (c + kGroupAlign - 1) & ~int64_t{kGroupAlign - 1};
+      g += t.cnt[e];
     }
     t.gstart[El] = g;
-    t.pstart[El] = q;
   }
   __syncthreads();
 }
 
-struct TransposeArgs {
-  const char* P;      // rows (ld bytes each); this rank's rows start at row base (at_send) or 0
-  int64_t ldp;
-  int at_send;
-  int64_t cols;       // C, multiple of 8
-  int64_t p_cap;      // rows of P
-  char* PT;           // (C, kt) bf16
-  int64_t kt;         // elements per PT row
-  const int32_t* send_counts;
-  const int32_t* recv_counts;
-  int ep_rank, local_experts;
-  int32_t* dev_err;
-  uint32_t* zero;     // n_zero words cleared by workgroup (0, 0): the weight-gradient counters
-  int64_t n_zero;
-};
-
-// PT[c][pstart[g] + i] = P[base + gstart[g] + i][c] for every local group g
-// and row i < count g, and zeros in the columns after each group up to the next
-// multiple of 64, so that a 16-byte K piece read past the group's last row
-// holds zeros. The work is cut into items: a 64-row block of one group (blocks
-// start at the group's first row, so the block's destination columns start on
-// a 128-byte line) times a 256-column tile. The grid holds as many workgroups
-// as fit on the chip at once, and workgroup x takes items x, x + grid, ...
-// (the host knows only a bound on the row blocks; the kernel counts them).
-// An item goes through one of two LDS buffers:
-// - every thread loads four 16-byte pieces along the rows and writes them to
-//   LDS, where 8-byte unit u of row r sits at unit u ^ 4 ((r / 8) ^ (r mod 8));
-// - every thread then reads 8 rows x 4 columns (eight 8-byte reads) and writes
-//   the 4 columns, 8 rows each, with 16-byte stores.
-// The swizzle puts the 16-byte writes of a quarter wave, the 8-byte reads of
-// a half wave at one row offset, and the 8 rows one lane reads (which the
-// compiler may pair into one instruction) on distinct banks. With two buffers
-// one barrier per item suffices: a buffer is written again only after every
-// thread has passed the following item's barrier, so has finished reading it.
-// The next item's loads are issued after the current item's stores, so that
-// waiting for them also covers the stores.
-constexpr int kTrCols = 256;  // columns per item; LDS rows of 512 bytes
-
-__global__ __launch_bounds__(512) void group_transpose_kernel(TransposeArgs p) {
-  __shared__ GroupTable t;
-  __shared__ int64_t s_bstart[kMaxLocalExperts + 1];
-  __shared__ __attribute__((aligned(16))) char tile_raw[2][64 * kTrCols * 2];
-  if (blockIdx.x == 0)
-    for (int64_t i = threadIdx.x; i < p.n_zero; i += blockDim.x) p.zero[i] = 0u;
-  load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
-  const int El = p.local_experts;
-  const int64_t n = t.gstart[El];
-  const int64_t base = p.at_send ? t.base : 0;
-  if (t.bad || base + n > p.p_cap || t.pstart[El] > p.kt) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
-    return;
-  }
-  if (threadIdx.x == 0) {
-    int64_t b = 0;
-    for (int e = 0; e < El; ++e) {
-      s_bstart[e] = b;
-      b += (t.cnt[e] + 63) / 64;
-    }
-    s_bstart[El] = b;
-  }
-  __syncthreads();
-  const int64_t ctiles = (p.cols + kTrCols - 1) / kTrCols;
-  const int64_t items = s_bstart[El] * ctiles;
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int lr = tid >> 5, ch = tid & 31;             // load: rows lr + 16 l, 16-byte piece ch
-  const int rg = lane & 7;                            // store: rows 8 rg .. 8 rg + 7,
-  const int cg = (tid >> 6) * 8 + (lane >> 3);        // columns 4 cg .. 4 cg + 3
-  const int pu = cg ^ (4 * rg);                       // their LDS unit, less the row term
-  struct Item {
-    int64_t c0, nr, src0, dst0;
-  };
-  auto locate = [&](int64_t it) {
-    const int64_t blk = it / ctiles;
-    int g = 0;
-    while (g + 1 < El && s_bstart[g + 1] <= blk) ++g;
-    const int64_t j64 = (blk - s_bstart[g]) * 64;     // first row of the block within group g
-    Item m;
-    m.c0 = (it - blk * ctiles) * kTrCols;
-    m.nr = t.cnt[g] - j64 < 64 ? t.cnt[g] - j64 : 64;
-    m.src0 = base + t.gstart[g] + j64;                // first source row
-    m.dst0 = t.pstart[g] + j64;                       // first destination column (64-aligned)
-    return m;
-  };
-  u32x4_t v[4];
-  auto load = [&](const Item& m) {
-    const int64_t gc = m.c0 + ch * 8;
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const int r = lr + 16 * l;
-      v[l] = zero_v4();
-      if (r < m.nr && gc < p.cols)
-        v[l] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(p.P + (m.src0 + r) * p.ldp + gc * 2));
-    }
-  };
-  int64_t it = blockIdx.x;
-  if (it >= items) return;
-  Item cur = locate(it);
-  load(cur);
-  for (int buf = 0; it < items; it += gridDim.x, buf ^= 1) {
-    lds_t* tb = (lds_t*)tile_raw[buf];
-#pragma unroll
-    for (int l = 0; l < 4; ++l) {
-      const int r = lr + 16 * l;
-      const int pch = ch ^ (2 * ((r >> 3) ^ (r & 7)));  // 16-byte piece: 8-byte units move in pairs
-      *reinterpret_cast<MC2_LDS u32x4_t*>(tb + r * (kTrCols * 2) + (pch << 4)) = v[l];
-    }
-    __syncthreads();
-    const Item m = cur;
-    if (m.c0 + 4 * cg < p.cols) {
-      uint64_t w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        w[i] = *reinterpret_cast<const MC2_LDS uint64_t*>(tb + (8 * rg + i) * (kTrCols * 2) +
-                                                          (pu ^ (4 * i)) * 8);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4_t o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t lo = static_cast<uint32_t>(w[2 * j] >> (16 * q)) & 0xffffu;
-          const uint32_t hi = static_cast<uint32_t>(w[2 * j + 1] >> (16 * q)) & 0xffffu;
-          o[j] = lo | (hi << 16);
-        }
-        // rows past the group's end were loaded as zeros: they pad the group
-        __builtin_nontemporal_store(
-            o, reinterpret_cast<u32x4_t*>(p.PT + ((m.c0 + 4 * cg + q) * p.kt + m.dst0 + 8 * rg) * 2));
-      }
-    }
-    if (it + gridDim.x < items) {
-      cur = locate(it + gridDim.x);
-      load(cur);
-    }
-  }
-}
-
-// Rows of one K slice of a weight-gradient tile: a group with more rows is
-// split into slices whose partial tiles are summed afterwards, so that one
-// large group does not set the length of the whole launch.
 constexpr int64_t kSliceRows = 4096;
 
 struct WgradArgs {
-  const char* PT;     // (M, kt) bf16: the transposed group rows
-  int64_t ldpt;       // bytes per PT row
+  const char* P;      // (rows, M) bf16, this rank's rows from row base (p_at_send) or 0
+  int64_t ldp;        // bytes per P row
+  int p_at_send;
+  int64_t p_cap;
   const char* Q;      // (rows, N) bf16, this rank's rows from row base (at_send) or 0
   int64_t ldq;
   int at_send;
@@ -565,27 +424,30 @@ struct WgradArgs {
 
 // dW[g] = P_g^T @ Q_g (M x N per local group g). Work unit = (group g, K
 // slice s, tile): a 256 x 256 tile over rows [s*L, min((s+1)*L, count g)) of
-// the group, L = kSliceRows; A is the group's column range of the transposed
-// workspace, B the group's rows of Q. Slices are numbered group by group, the
-// groups with most rows first (so the longest units are dispatched first and
-// the short ones fill the end of the launch). Workgroup b runs on XCD b % 8,
-// and each XCD takes q tiles of every slice, slice after slice: the XCDs get
-// the same unit lengths, so none of them is left with the long units while
-// the others idle (numbering units in order and giving each XCD a run of 32
-// put the longest of every round on the same XCD). An XCD's q tiles of a
-// slice form a bm x bn block where the tile grid splits into 8 such blocks,
-// so that they share A and B slabs in that XCD's L2; else a run of q tiles in
-// row-fastest order. A group of one slice stores its tile (non-temporal: the result is not read
-// again here; the same hint on the partials below, which are read back, was
-// slower); for a split group every slice stores its partial tile in its slot,
-// and the last slice to finish a tile (counted with an agent-scope release /
-// acquire, as the ready flags) sums the partials in slice order, so the result
-// does not depend on timing. An empty group gets zeros. The grid may have more
-// workgroups than units (the host knows only a bound); the rest exit.
-// KT: the K extent of a unit may end inside a stage (four-wave tiles; the
-// eight-wave loop always checks).
+// the group, L = kSliceRows. Both operands are the group's rows as they lie
+// (P's rows for A, Q's for B), read k-major by the main loop: no transposed
+// copy is made. Slices are numbered group by group, the groups with most rows
+// first (so the longest units are dispatched first and the short ones fill
+// the end of the launch). Workgroup b runs on XCD b % 8, and each XCD takes q
+// tiles of every slice, slice after slice: the XCDs get the same unit
+// lengths, so none of them is left with the long units while the others idle
+// (numbering units in order and giving each XCD a run of 32 put the longest
+// of every round on the same XCD). An XCD's q tiles of a slice form a
+// bm x bn block where the tile grid splits into 8 such blocks, so that they
+// share A and B slabs in that XCD's L2; else a run of q tiles in row-fastest
+// order. A group of one slice stores its tile (non-temporal: the result is
+// not read again here; the same hint on the partials below, which are read
+// back, was slower); for a split group every slice stores its partial tile in
+// its slot, and the last slice to finish a tile (counted with an agent-scope
+// release / acquire, as the ready flags) sums the partials in slice order, so
+// the result does not depend on timing. An empty group gets zeros. The grid
+// may have more workgroups than units (the host knows only a bound); the
+// rest exit. The tile counters start at zero: the input-gradient launch
+// before this one clears them.
+// KT: the K extent of a unit may end inside a stage.
 template <class TS, bool KT>
 __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
+  static_assert(TS::NW == 4 && TS::BM == 256, "four-wave 256-row tiles (row-major A)");
   constexpr int kSmem = TS::kStages * TS::kStageBytes;
   __shared__ __attribute__((aligned(16))) char smem_raw[kSmem];
   __shared__ GroupTable t;
@@ -619,7 +481,9 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   }
   __syncthreads();
   const int64_t base = p.at_send ? uni(t.base) : 0;
-  if (t.bad || base + t.gstart[El] > p.q_cap || s_slot[El] > p.max_slots) {
+  const int64_t pbase = p.p_at_send ? uni(t.base) : 0;
+  if (t.bad || base + t.gstart[El] > p.q_cap || pbase + t.gstart[El] > p.p_cap ||
+      s_slot[El] > p.max_slots) {
     if (threadIdx.x == 0 && blockIdx.x == 0) atomic_or_err(p.dev_err, MC2_DEVERR_COUNTS);
     return;
   }
@@ -650,7 +514,7 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   const int64_t col0 = static_cast<int64_t>(tn) * TS::BN;
   const int64_t cnt = uni(static_cast<int64_t>(t.cnt[g]));
   const int64_t nslices = uni(s_sstart[q + 1]) - uni(s_sstart[q]);
-  const int64_t gstart = uni(t.gstart[g]), pstart = uni(t.pstart[g]);
+  const int64_t gstart = uni(t.gstart[g]);
   float* dst = p.out + static_cast<int64_t>(g) * p.M * p.N;
   const int64_t nrows = p.M - row0, ncols = p.N - col0;
   if (cnt == 0) {
@@ -667,30 +531,19 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   f32x4_t acc[TS::FM][TS::FN];
   BDesc bd{p.Q + (base + gstart + k0) * p.ldq, p.ldq, p.N};
   PlainCols cm{col0, p.N - 8};
-  if constexpr (TS::NW == 4)
-    mainloop_w4<Elem::BF16, false, TS, KT>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1,
-                                           bd, col0, cm, ks, acc);
-  else
-    mainloop<Elem::BF16, false, TS>(smem, p.PT + (pstart + k0) * 2, p.ldpt, row0, p.M - 1, bd,
-                                    col0, cm, ks, acc);
+  // A = the group's rows of P, read k-major (row-major (k, m)) like B
+  mainloop_w4<Elem::BF16, false, TS, KT, true>(smem, p.P + (pbase + gstart + k0) * p.ldp, p.ldp,
+                                               row0, p.M - 1, bd, col0, cm, ks, acc);
   if (nslices == 1) {
     char* base_out = reinterpret_cast<char*>(dst + row0 * p.N + col0);
-    if constexpr (TS::NW == 4) {
-      // runs of four columns (N is a multiple of 8): one 16-byte store each
-      epilogue_quads<Elem::BF16, TS, Out::F32>(
-          acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr,
-          [&](int r, int c, const auto& v) {
-            if (r < nrows && c < ncols)
-              __builtin_nontemporal_store(pack4<Out::F32>(v),
-                                          reinterpret_cast<u32x4_t*>(base_out + (r * p.N + c) * 4));
-          });
-    } else {
-      epilogue_linear<Elem::BF16, TS, Out::F32>(
-          acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr, [&](int r, int c, float v) {
-            if (r < nrows && c < ncols)
-              __builtin_nontemporal_store(v, reinterpret_cast<float*>(base_out + (r * p.N + c) * 4));
-          });
-    }
+    // runs of four columns (N is a multiple of 8): one 16-byte store each
+    epilogue_quads<Elem::BF16, TS, Out::F32>(
+        acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr, nullptr,
+        [&](int r, int c, const auto& v) {
+          if (r < nrows && c < ncols)
+            __builtin_nontemporal_store(pack4<Out::F32>(v),
+                                        reinterpret_cast<u32x4_t*>(base_out + (r * p.N + c) * 4));
+        });
     return;
   }
   // split group: this slice's partial tile (dense BM x BN) into its slot
@@ -698,17 +551,11 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   float* part0 = p.partials + (uni(s_slot[g]) * per_group + lt) * kTileElems;
   const int64_t slice_stride = per_group * kTileElems;
   char* mine = reinterpret_cast<char*>(part0 + s * slice_stride);
-  if constexpr (TS::NW == 4)
-    epilogue_quads<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                             nullptr, [&](int r, int c, const auto& v) {
-                                               *reinterpret_cast<u32x4_t*>(mine + (r * TS::BN + c) * 4) =
-                                                   pack4<Out::F32>(v);
-                                             });
-  else
-    epilogue_linear<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
-                                              nullptr, [&](int r, int c, float v) {
-                                                put_out_global<Out::F32>(mine + (r * TS::BN + c) * 4, v);
-                                              });
+  epilogue_quads<Elem::BF16, TS, Out::F32>(acc, row0, p.M - 1, col0, p.N, nullptr, 0.f, nullptr,
+                                           nullptr, [&](int r, int c, const auto& v) {
+                                             *reinterpret_cast<u32x4_t*>(mine + (r * TS::BN + c) * 4) =
+                                                 pack4<Out::F32>(v);
+                                           });
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   uint32_t* ctr = p.counters + static_cast<int64_t>(g) * per_group + lt;
@@ -857,33 +704,34 @@ extern "C" int mc2_gmm_combine(const void* h, int64_t h_rows, const int32_t* rec
 
 namespace mc2 {
 
-// Elements per row of the transposed workspace: every group padded to 64,
-// and the row pitch a multiple of 128 bytes.
-static int64_t backward_kt(int64_t rows, int local_experts) {
-  return (rows + kGroupAlign * static_cast<int64_t>(local_experts) + kGroupAlign - 1) &
-         ~int64_t{kGroupAlign - 1};
-}
-
 // Workspace of a weight gradient dW = P^T Q over `rows` rows of P, dW (E_l,
-// M, N): the transposed rows (M x kt bf16), then the tile counters, then the
-// partial-tile slots of split groups. A split group of c > L rows has
-// ceil(c / L) < 2c / L slices, so 2 * rows / L slots always suffice.
+// M, N): the tile counters, then the partial-tile slots of split groups. A
+// split group of c > L rows has ceil(c / L) < 2c / L slices, so 2 * rows / L
+// slots always suffice.
 struct WgradLayout {
-  int64_t kt, tiles_m, tiles_n, max_slots;
+  int64_t tiles_m, tiles_n, max_slots;
   size_t off_ctr, off_part, total;
 };
 
 static WgradLayout wgrad_layout(int64_t rows, int local_experts, int64_t M, int64_t N) {
   WgradLayout w{};
-  w.kt = backward_kt(rows, local_experts);
   w.tiles_m = (M + TileL::BM - 1) / TileL::BM;
   w.tiles_n = (N + TileL::BN - 1) / TileL::BN;
   w.max_slots = 2 * rows / kSliceRows;
   const size_t per_group = static_cast<size_t>(w.tiles_m * w.tiles_n);
-  w.off_ctr = (static_cast<size_t>(M) * static_cast<size_t>(w.kt) * 2 + 255) & ~size_t{255};
-  w.off_part = (w.off_ctr + per_group * local_experts * 4 + 255) & ~size_t{255};
+  w.off_ctr = 0;
+  w.off_part = (per_group * local_experts * 4 + 255) & ~size_t{255};
   w.total = w.off_part + static_cast<size_t>(w.max_slots) * per_group * TileL::BM * TileL::BN * 4;
   return w;
+}
+
+// The tile counters of the weight gradient, for the input-gradient launch
+// before it to clear.
+static void clear_counters(GroupedArgs& a, void* workspace, int64_t rows, int local_experts,
+                           int64_t M, int64_t N) {
+  const WgradLayout L = wgrad_layout(rows, local_experts, M, N);
+  a.zero = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + L.off_ctr);
+  a.n_zero = L.tiles_m * L.tiles_n * local_experts;
 }
 
 static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, const char* Q,
@@ -894,35 +742,11 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   const WgradLayout L = wgrad_layout(p_cap, local_experts, M, N);
   char* ws = static_cast<char*>(workspace);
   const int64_t per_group = L.tiles_m * L.tiles_n;
-  TransposeArgs t{};
-  t.P = P;
-  t.ldp = ldp;
-  t.at_send = p_at_send;
-  t.cols = M;
-  t.p_cap = p_cap;
-  t.PT = ws;
-  t.kt = L.kt;
-  t.send_counts = send_counts;
-  t.recv_counts = recv_counts;
-  t.ep_rank = ep_rank;
-  t.local_experts = local_experts;
-  t.dev_err = dev_err;
-  t.zero = reinterpret_cast<uint32_t*>(ws + L.off_ctr);
-  t.n_zero = per_group * local_experts;
-  // items: 64-row blocks, each inside one group (at most rows / 64 + E_l of
-  // them), times 256-column tiles; two workgroups fit on a CU (LDS), and the
-  // grid holds that many, or fewer when there are fewer items
-  const int64_t rb = p_cap / 64 + local_experts;
-  const int64_t items = rb * ((M + kTrCols - 1) / kTrCols);
-  int64_t gx = 2 * static_cast<int64_t>(num_cus());
-  gx = gx < items ? gx : items;
-  gx = gx < 1 ? 1 : gx;
-  hipLaunchKernelGGL(group_transpose_kernel, dim3(static_cast<unsigned>(gx)),
-                     dim3(512), 0, stream, t);
-  if (hipGetLastError() != hipSuccess) return MC2_ERR_HIP;
   WgradArgs w{};
-  w.PT = ws;
-  w.ldpt = L.kt * 2;
+  w.P = P;
+  w.ldp = ldp;
+  w.p_at_send = p_at_send;
+  w.p_cap = p_cap;
   w.Q = Q;
   w.ldq = ldq;
   w.at_send = q_at_send;
@@ -941,7 +765,7 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
       continue;
     if (!w.bm || a + b < w.bm + w.bn) w.bm = a, w.bn = b;
   }
-  w.counters = t.zero;
+  w.counters = reinterpret_cast<uint32_t*>(ws + L.off_ctr);
   w.partials = reinterpret_cast<float*>(ws + L.off_part);
   w.max_slots = L.max_slots;
   w.send_counts = send_counts;
@@ -987,8 +811,7 @@ extern "C" int mc2_gmm_combine_backward(const void* dy_buf, int64_t dy_rows,
   if (!workspace) return MC2_ERR_NULL;
   if (!aligned16(workspace)) return MC2_ERR_ALIGN;
   if (ws_bytes < mc2_gmm_backward_workspace_size(h_rows, local_experts, I, H)) return MC2_ERR_WORKSPACE;
-  if (!offsets_fit(H * 2, H * 2) || !offsets_fit(backward_kt(h_rows, local_experts) * 2, H * 2))
-    return MC2_ERR_UNSUPPORTED;
+  if (!offsets_fit(H * 2, H * 2) || !offsets_fit(I * 2, H * 2)) return MC2_ERR_UNSUPPORTED;
   // dgrad: dA = dY_g @ w2[g]^T, the weight read as (I, H) rows; SwiGLU backward fused
   GroupedArgs a{};
   a.A = static_cast<const char*>(dy_buf);
@@ -1016,6 +839,7 @@ extern "C" int mc2_gmm_combine_backward(const void* dy_buf, int64_t dy_rows,
   a.ldg = 2 * I * 2;
   const int64_t rows = dy_rows < h_rows ? dy_rows : h_rows;
   const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((I + TileG::BN - 1) / TileG::BN);
+  clear_counters(a, workspace, h_rows, local_experts, I, H);
   st = glu ? run_grouped<kSwigluBwd, true>(a, max_tiles, stream)
            : run_grouped<kLinear, true>(a, max_tiles, stream);
   if (st) return st;
@@ -1045,8 +869,7 @@ extern "C" int mc2_gmm_dispatch_backward(const void* dg, int64_t dg_rows, const 
   if (!aligned16(workspace)) return MC2_ERR_ALIGN;
   if (ws_bytes < mc2_gmm_backward_workspace_size(send_rows, local_experts, H, I2))
     return MC2_ERR_WORKSPACE;
-  if (!offsets_fit(I2 * 2, I2 * 2) || !offsets_fit(backward_kt(send_rows, local_experts) * 2, I2 * 2))
-    return MC2_ERR_UNSUPPORTED;
+  if (!offsets_fit(I2 * 2, I2 * 2) || !offsets_fit(H * 2, I2 * 2)) return MC2_ERR_UNSUPPORTED;
   // dgrad: dX_g = dG_g @ w1[g]^T, the weight read as (H, I2) rows, written at the send rows
   GroupedArgs a{};
   a.A = static_cast<const char*>(dg);
@@ -1072,6 +895,7 @@ extern "C" int mc2_gmm_dispatch_backward(const void* dg, int64_t dg_rows, const 
   a.ktiles = static_cast<int>((I2 + 63) / 64);
   const int64_t rows = dg_rows < dx_rows ? dg_rows : dx_rows;
   const int64_t max_tiles = (rows / TileG::BM + local_experts) * ((H + TileG::BN - 1) / TileG::BN);
+  clear_counters(a, workspace, send_rows, local_experts, H, I2);
   st = run_grouped<kLinear, true>(a, max_tiles, stream);
   if (st) return st;
   // wgrad: dW1[g] = R_g^T @ dG_g over this rank's send rows R

@@ -415,9 +415,9 @@ int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermu
  * caller-owned, 16-byte aligned, at least
  * mc2_gmm_backward_workspace_size(rows, E_l, M, N) bytes with (rows, M, N) =
  * (h_rows, I, H) for the combine backward and (send_rows, H, I2) for the
- * dispatch backward (the rows transposed, each expert padded to 64, tile
- * counters and partial tiles); no initialisation needed. Constraints: I, H,
- * I2 multiples of 8.
+ * dispatch backward (tile counters and partial tiles; the weight gradient
+ * reads h and the send rows in place); no initialisation needed. Constraints:
+ * I, H, I2 multiples of 8.
  */
 size_t mc2_gmm_backward_workspace_size(int64_t rows, int local_experts, int64_t M, int64_t N);
 

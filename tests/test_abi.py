@@ -189,13 +189,12 @@ def test_mm_ar_validates(lib):
 
 
 def test_gmm_backward_validates(lib):
-    # transposed rows (each expert padded to 64), counters, no split slots below 2048 rows
+    # tile counters (3 x 8 tiles x 16 experts, 256-byte aligned), no split slots below 2048 rows
     ws = lib.mc2_gmm_backward_workspace_size(1000, 16, 768, 2048)
-    pt = 768 * ((1000 + 64 * 16 + 63) // 64 * 64) * 2
-    assert ws == (pt + 255) // 256 * 256 + (3 * 8 * 16 * 4 + 255) // 256 * 256
+    assert ws == (3 * 8 * 16 * 4 + 255) // 256 * 256
+    # then 2 * rows / 4096 slots of 256 x 256 fp32 partial tiles per tile of an expert
     big = lib.mc2_gmm_backward_workspace_size(40000, 16, 768, 2048)
-    pt = 768 * ((40000 + 64 * 16 + 63) // 64 * 64) * 2
-    assert big == (pt + 255) // 256 * 256 + 1536 + (2 * 40000 // 4096) * 24 * 256 * 256 * 4
+    assert big == 1536 + (2 * 40000 // 4096) * 24 * 256 * 256 * 4
     assert lib.mc2_gmm_backward_workspace_size(1000, 0, 768, 64) == 0
     Cb = lib.mc2_gmm_combine_backward
     base = (FAKE, 100, FAKE, FAKE, 1, 0, 16, 4, FAKE, 64, 128, FAKE, 100)

@@ -181,7 +181,8 @@ def test_c4_backward_full_size_sampled():
 def test_weight_gradient_split_groups_deterministic():
     """Groups of 5000 and 9000 rows (2 and 3 slices of 4096 rows, partial tiles
     summed in slice order) plus an empty one: the whole dW1 and dW2 against
-    the oracle, and a second call gives the same bits."""
+    the oracle, and a second call gives the same bits, with workspaces whose
+    every byte is 0xff (the tile counters are cleared by the call itself)."""
     H, I = 264, 136
     send_counts = np.array([5000, 0, 9000], dtype=np.int32)
     recv = send_counts.copy()
@@ -195,11 +196,15 @@ def test_weight_gradient_split_groups_deterministic():
     dx = torch.zeros((n, H), dtype=torch.bfloat16, device="cuda")
     err = torch.zeros(1, dtype=torch.int32, device="cuda")
     outs = []
-    for _ in range(2):
+    dirty = lambda m, nn: torch.full((mc2.mc2_gmm_backward_workspace_size(n, 3, m, nn),), 0xFF,
+                                     dtype=torch.uint8, device="cuda")
+    for call in range(2):
         _, dw2 = mc2.mc2_gmm_combine_backward(dev["dy"], rc, sc, w2, dev["h"], ep_rank=0,
-                                              num_experts=3, dev_err=err)
+                                              num_experts=3, dev_err=err,
+                                              workspace=dirty(I, H) if call else None)
         _, dw1 = mc2.mc2_gmm_dispatch_backward(dev["dg"], rc, sc, w1, dev["send"], dx, ep_rank=0,
-                                               num_experts=3, dev_err=err)
+                                               num_experts=3, dev_err=err,
+                                               workspace=dirty(H, 2 * I) if call else None)
         torch.cuda.synchronize()
         outs.append((dw1.cpu().numpy(), dw2.cpu().numpy()))
     assert err.item() == 0
@@ -213,12 +218,13 @@ def test_weight_gradient_split_groups_deterministic():
     _assert_wgrad(outs[0][0], ref_dw1, _dec(b["send"]), _dec(b["dg"]), recv, "split dW1")
 
 
-def test_weight_gradient_many_transpose_items_ragged_columns():
-    """40011 rows in ragged groups with H = 264 (a 256-column tile plus an
-    8-column one) and I = 136: the token-major operands are transposed in
-    more 64-row x 256-column items than the grid has workgroups, so each
-    workgroup walks several items through both LDS buffers, partial column
-    tiles included. The whole dW1 and dW2 against the oracle."""
+def test_weight_gradient_long_ragged_groups_ragged_tiles():
+    """40011 rows in ragged groups (17001 and 22943 rows: several 4096-row
+    slices each, the last ending inside a K stage; groups of 3 and 64 rows)
+    with H = 264 (a 256-wide tile plus an 8-wide one, for the rows of dW1 and
+    the columns of dW2) and I = 136: both operands are read in place, k-major,
+    with the clamped last 16-byte piece at the ragged edges. The whole dW1 and
+    dW2 against the oracle."""
     H, I = 264, 136
     send_counts = np.array([17001, 3, 0, 64, 22943], dtype=np.int32)
     recv = send_counts.copy()
