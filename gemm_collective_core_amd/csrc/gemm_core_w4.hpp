@@ -21,17 +21,17 @@
 //
 // One wave issues everything in one stream, so the stage is a fixed
 // interleave of its 2 x 64 MFMAs (16 cycles each) with the memory
-// instructions, one memory instruction after an MFMA at most, so that a load
-// the memory pipeline is slow to take stalls the wave for at most the MFMA's
-// own latency:
-//   k-step 0, MFMA slots 0..63: the 16 operand reads of k-step 1 after the
-//     first 16 MFMAs; at slot kBar the wave waits for them and for its own
-//     loads of the next stage, and the workgroup barrier follows (every wave
-//     is done with this stage's buffer and every load of the next stage has
-//     landed); then the loads of the stage after next into the buffer just
-//     released, one every second slot;
-//   k-step 1, slots 64..127: the 16 operand reads of the next stage's k-step
-//     0, one every second slot.
+// instructions, at most one LDS read and one load after an MFMA, so that a
+// memory instruction the pipeline is slow to take stalls the wave for at most
+// the MFMA's own latency:
+//   the first slots: the operand reads of k-step 1;
+//   slot kBarA: the wave waits for them, and a workgroup barrier follows
+//     (every wave is done with this stage's buffer);
+//   from there to the stage's last slot: the loads of the stage after next
+//     into the buffer just released, evenly spread;
+//   slot kBarB (in k-step 1): the wave waits for its loads of the next
+//     stage, and a barrier follows (every wave's have landed);
+//   after it: the operand reads of the next stage's k-step 0.
 // Every LDS read is inline assembly (the compiler would otherwise wait for
 // all loads before any LDS read); each k-step begins with an lgkmcnt(0) wait
 // for the reads issued during the previous one.
@@ -152,19 +152,30 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   //   q < NR        the k-step-1 operand reads of this stage;
   //   kBarA         wait for them, barrier: this stage's buffer is free;
   //   load slots    the loads of the stage after next into that buffer,
-  //                 spread evenly up to kBarB so that the CU's load path
-  //                 (about one 1 KiB load per 18 cycles) never queues them;
-  //   kBarB         wait for this wave's loads of the next stage, barrier;
-  //   after kBarB   the next stage's k-step-0 operand reads.
+  //                 spread evenly over the rest of the stage (kBarA + 1 to
+  //                 the last slot), so that the CU's load path (about one
+  //                 1 KiB load per 18 cycles, shared by the four waves)
+  //                 never queues them;
+  //   kBarB         wait for this wave's loads of the next stage (those of
+  //                 the stage after next issued before kBarB may still be in
+  //                 flight: loads complete in order), barrier;
+  //   after kBarB   the next stage's k-step-0 operand reads, and the rest of
+  //                 the loads.
   constexpr int kBarA = NR + 4;
   constexpr int kBarB = 2 * MM - NR - 4;
-  constexpr int kLSpan = kBarB - kBarA - 1;
+  constexpr int kLSpan = 2 * MM - kBarA - 2;  // load slots kBarA + 1 .. 2 MM - 1
   static_assert(kLSpan >= NL && kBarB + NR < 2 * MM, "slots for the loads and the reads");
   const int tid = threadIdx.x, lane = tid & 63;
   // the wave index as a wave-uniform value: the LDS destinations of the loads
   // (M0) are then scalar arithmetic
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto load_index = [](int q) constexpr { return load_slot_index(q, kBarA, kLSpan, NL); };
+  // loads of the stage after next issued before kBarB
+  constexpr int kLoadsBeforeB = [] {
+    int c = 0;
+    for (int j = 0; j < NL; ++j) c += kBarA + 1 + (j * kLSpan) / NL < kBarB;
+    return c;
+  }();
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
 
@@ -399,12 +410,10 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
         lgkm_wait(0);  // every read of this stage's buffer is done
         bar_sync();    // ... by every wave: the buffer may be refilled
         nx = prep();  // stage it + 2
-      } else if constexpr (load_index(q) >= 0) {
-        issue_j(nx, load_index(q));
       } else if constexpr (q == kBarB) {
-        // this wave's loads of the next stage have landed (the NL loads of
-        // the stage after next, issued since kBarA, may still be in flight)
-        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NL) : "memory");
+        // this wave's loads of the next stage have landed (those of the
+        // stage after next issued since kBarA may still be in flight)
+        asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kLoadsBeforeB) : "memory");
         bar_sync();  // ... and every wave's
       } else if constexpr (q > kBarB && (q - kBarB - 1) < NR) {
         // the next stage's k-step-0 operands (after the last stage: reads of
@@ -412,6 +421,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
         read_op(std::integral_constant<int, q - kBarB - 1>{}, std::integral_constant<int, 1 - P>{},
                 I0{}, a0, b0);
       }
+      if constexpr (load_index(q) >= 0) issue_j(nx, load_index(q));
       __builtin_amdgcn_sched_barrier(0);
     });
   };
