@@ -399,7 +399,23 @@ __device__ __forceinline__ void load_group_table(GroupTable& t, const int32_t* s
   __syncthreads();
 }
 
-constexpr int64_t kSliceRows = 4096;
+constexpr int64_t kSliceRows = 4096;  // the shortest slice (workspace and grid bounds)
+
+// Slice length L for N local rows over tiles_per_group tiles per expert on
+// `cus` CUs: the rows of K per CU if the work were spread evenly, rounded down
+// to a multiple of 2048, and at least kSliceRows. Longer slices mean fewer
+// partial tiles and fixed costs, shorter ones a finer balance; on the MoE
+// workload (40289 rows) this gives 4096 for fc2's 24 tiles per expert and
+// 6144 for fc1's 48, the best of 3072 .. 8192 measured for each.
+// (In single precision with the hardware reciprocal: a heuristic, computed
+// the same way by every workgroup, and no 64-bit division.)
+__device__ __forceinline__ int64_t slice_rows(int64_t n, int tiles_per_group, int cus) {
+  const float per_cu = static_cast<float>(n) * static_cast<float>(tiles_per_group) *
+                       __builtin_amdgcn_rcpf(static_cast<float>(cus > 0 ? cus : 1));
+  const float blocks = per_cu * (1.0f / 2048.0f);
+  const int64_t l = blocks < 1e6f ? static_cast<int64_t>(blocks) * 2048 : int64_t{1} << 31;
+  return l > kSliceRows ? l : kSliceRows;
+}
 
 struct WgradArgs {
   const char* P;      // (rows, M) bf16, this rank's rows from row base (p_at_send) or 0
@@ -414,6 +430,7 @@ struct WgradArgs {
   int64_t M, N;
   int tiles_m, tiles_n;
   int q;              // units per XCD per slice: ceil(tiles_m * tiles_n / 8)
+  int cus;            // compute units (for the slice length)
   int bm, bn;         // an XCD's q tiles of a slice as a bm x bn block (bm = 0: a run of q)
   uint32_t* counters; // E_l * tiles_m * tiles_n, zero on entry (left zero)
   float* partials;    // max_slots slices' partial tiles of split groups
@@ -426,7 +443,7 @@ struct WgradArgs {
 
 // dW[g] = P_g^T @ Q_g (M x N per local group g). Work unit = (group g, K
 // slice s, tile): a 256 x 256 tile over rows [s*L, min((s+1)*L, count g)) of
-// the group, L = kSliceRows. Both operands are the group's rows as they lie
+// the group, L = slice_rows(local rows, ...). Both operands are the group's rows as they lie
 // (P's rows for A, Q's for B), read k-major by the main loop: no transposed
 // copy is made. Slices are numbered group by group, the groups with most rows
 // first (so the longest units are dispatched first and the short ones fill
@@ -456,6 +473,7 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
   __shared__ int64_t s_sstart[kMaxLocalExperts + 1];  // first slice, by position in the order
   __shared__ int64_t s_slot[kMaxLocalExperts + 1];    // by group
   __shared__ int s_order[kMaxLocalExperts];           // position -> group
+  __shared__ int s_ns[kMaxLocalExperts];              // slices, by group
   __shared__ int s_last;
   lds_t* smem = (lds_t*)smem_raw;
   load_group_table(t, p.send_counts, p.recv_counts, p.ep_rank, p.local_experts);
@@ -468,11 +486,19 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
     s_order[rank] = e;
   }
   __syncthreads();
+  const int64_t L = uni(slice_rows(t.gstart[El], per_group, p.cus));
+  // slices per group, one group per thread (32-bit: counts are int32 and
+  // L < 2^31)
+  for (int e = threadIdx.x; e < El; e += TS::NT) {
+    const uint32_t c = static_cast<uint32_t>(t.cnt[e]), l = static_cast<uint32_t>(L);
+    s_ns[e] = c > l ? static_cast<int>((c + l - 1) / l) : 1;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     int64_t sl = 0, slot = 0;
     for (int q = 0; q < El; ++q) {
       const int e = s_order[q];
-      const int64_t ns = t.cnt[e] > kSliceRows ? (t.cnt[e] + kSliceRows - 1) / kSliceRows : 1;
+      const int64_t ns = s_ns[e];
       s_sstart[q] = sl;
       s_slot[e] = slot;
       sl += ns;
@@ -526,8 +552,8 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
     }
     return;
   }
-  const int64_t k0 = static_cast<int64_t>(s) * kSliceRows;
-  const int64_t klen = cnt - k0 < kSliceRows ? cnt - k0 : kSliceRows;
+  const int64_t k0 = static_cast<int64_t>(s) * L;
+  const int64_t klen = cnt - k0 < L ? cnt - k0 : L;
   const int ktiles = static_cast<int>((klen + 63) / 64);
   KSpan ks{klen, 0, 0, ktiles, ktiles};
   f32x4_t acc[TS::FM][TS::FN];
@@ -761,6 +787,7 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   // q tiles of each slice per XCD; the block shape with the fewest A and B
   // slabs (bm + bn) among those that cut the tile grid into 8 blocks
   w.q = static_cast<int>((per_group + 7) / 8);
+  w.cus = static_cast<int>(num_cus());
   for (int a = 1; a <= w.q; ++a) {
     const int b = w.q / a;
     if (a * b != w.q || L.tiles_m % a || L.tiles_n % b || (L.tiles_m / a) * (L.tiles_n / b) != 8)
@@ -776,6 +803,7 @@ static int run_wgrad(const char* P, int64_t ldp, int p_at_send, int64_t p_cap, c
   w.local_experts = local_experts;
   w.dev_err = dev_err;
   // at most rows / L + E_l slices in all, q units of each per XCD
+  // (L >= kSliceRows, so these bound the slices of any slice length)
   const int64_t units = (p_cap / kSliceRows + local_experts) * 8 * w.q;
   if (units > 0x3fffffff) return MC2_ERR_SHAPE;
   hipLaunchKernelGGL((wgrad_kernel<TileW, true>), dim3(static_cast<unsigned>(units)),

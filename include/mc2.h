@@ -409,9 +409,11 @@ int mc2_moe_unpermute(const void* y_full, int64_t y_rows, const int32_t* unpermu
  * the forward: w2 (E_l, I, H), w1 (E_l, H, I2), bf16. Counts
  * and their checks as for mc2_gmm_dispatch (MC2_DEVERR_COUNTS, nothing
  * computed, on a mismatch or when rows exceed a buffer). An expert with no
- * rows gets a zero weight gradient. A weight gradient over more than 4096
- * rows of one expert is split into slices of 4096 rows whose partial tiles are
- * summed in slice order (the result does not depend on timing). workspace:
+ * rows gets a zero weight gradient. A weight gradient over more than L rows
+ * of one expert is split into slices of L rows whose partial tiles are summed
+ * in slice order (the result does not depend on timing); L is the local rows
+ * times the output tiles per expert (256 x 256) over the CUs, rounded down to
+ * a multiple of 2048, and at least 4096. workspace:
  * caller-owned, 16-byte aligned, at least
  * mc2_gmm_backward_workspace_size(rows, E_l, M, N) bytes with (rows, M, N) =
  * (h_rows, I, H) for the combine backward and (send_rows, H, I2) for the
