@@ -100,10 +100,19 @@ struct GluCols {
   }
 };
 
+// The SwiGLU backward epilogue (below) works in quarters of 64 rows: fp32 dA
+// rows (padded) and then the bf16 gate / up rows.
+constexpr int kSbQRows = 64;
+
+template <class TS>
+constexpr int swiglu_bwd_smem() {
+  return kSbQRows * (TS::BN * 4 + 16) + kSbQRows * TS::BN * 4;
+}
+
 template <class TS, int MODE>
 constexpr int grouped_smem() {
-  // kSwigluBwd stages fp32 values, half a tile's rows at a time
-  constexpr int stage = MODE == kSwigluBwd ? (TS::BM / 2) * (TS::BN * 4 + 16)
+  // kSwigluBwd stages 64 rows of fp32 dA and of gate / up at a time
+  constexpr int stage = MODE == kSwigluBwd ? swiglu_bwd_smem<TS>()
                                            : TS::BM * ((MODE == kSwiglu ? TS::BN / 2 : TS::BN) * 2 + 16);
   return TS::kStages * TS::kStageBytes > stage ? TS::kStages * TS::kStageBytes : stage;
 }
@@ -114,46 +123,82 @@ constexpr int grouped_smem() {
 // (gate in columns [0, inter), up in [inter, 2 inter)):
 //   d_gate = dA * up * s * (1 + gate * (1 - s)),  d_up = dA * gate * s,
 //   s = 1 / (1 + exp(-gate)),
-// written as bf16 to the same columns of `out`. dA goes through LDS in fp32,
-// half the tile's rows at a time, so that every thread then handles 8
-// consecutive columns with 16-byte loads and stores.
+// written as bf16 to the same columns of `out`. The tile goes in quarters of
+// 64 rows: dA into LDS in fp32, and the quarter's gate and up rows (1 KiB per
+// row) into LDS with loads straight to LDS, all in flight at once; after one
+// wait every thread handles 8 consecutive columns of a row from LDS and
+// stores them with 16-byte stores. (Loading gate and up into registers
+// piece by piece made every piece wait for the stores before it, which share
+// the wait counter with the loads.)
 template <class TS>
 __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (&acc)[TS::FM][TS::FN],
                                                     const GroupedArgs& p, int64_t orow0,
                                                     int64_t nrows, int64_t ocol0) {
-  constexpr int HR = TS::BM / 2;
-  constexpr int pitch = TS::BN * 4 + 16;
-  constexpr int CPR = TS::BN / 8;  // 8-column pieces per row
-  static_assert(TS::WTM == HR, "each wave's rows must lie in one half");
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int QR = kSbQRows;
+  constexpr int NQ = TS::BM / QR;
+  constexpr int pitch = TS::BN * 4 + 16;  // fp32 dA row
+  constexpr int GROW = TS::BN * 4;        // gate then up, bf16: one 1 KiB load per row
+  constexpr int GB = QR * pitch;          // gate / up rows after the dA rows
+  constexpr int CPR = TS::BN / 8;         // 8-column pieces per row
+  static_assert(TS::NW == 4 && TS::BN == 256 && GROW == 1024, "1 KiB gate / up rows");
+  static_assert(TS::WTM % QR == 0 && QR % (TS::NW * 4) == 0, "quarters inside one wave row");
+  // The thread index through an assembly move: what is derived from it is
+  // then computed here, after the main loop, and not kept live through it
+  // (the compiler would hoist it and spill).
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(static_cast<int>(threadIdx.x)));
+  const int lane = tid & 63, wave = tid >> 6;
   const int wrow0 = (wave / TS::WN) * TS::WTM;
   const int wcol0 = (wave % TS::WN) * TS::WTN;
-  for (int half = 0; half < 2; ++half) {
-    __syncthreads();
-    if (wrow0 == half * HR) {
-      // runs of four columns per lane (AccLayout of the four-wave tiles)
-      static_assert(AccLayout<TS>::kRowRuns, "runs of four columns");
+  // lane l of a row load: gate (l < 32) or up, 8 columns from ocol0 + 8 (l & 31)
+  const int64_t gcol = ocol0 + 8 * (lane & 31);
+  const bool col_ok = gcol < p.inter;
+  const uint32_t coff = static_cast<uint32_t>(((lane >> 5) ? p.inter + gcol : gcol) * 2);
+  for (int q = 0; q < NQ; ++q) {
+    __syncthreads();  // every read of the previous quarter's LDS rows is done
+    // dA of the quarter: the fragment rows fm0 .. fm0 + 3 of the waves whose
+    // rows hold it (a compile-time choice per quarter: the accumulators are
+    // registers)
+    sfor<NQ>([&](auto Qc) {
+      constexpr int qq = decltype(Qc)::value;
+      constexpr int fm0 = (qq * QR % TS::WTM) / 16;
+      if (q == qq && wrow0 == qq * QR / TS::WTM * TS::WTM) {
+        // runs of four columns per lane (AccLayout of the four-wave tiles)
+        static_assert(AccLayout<TS>::kRowRuns, "runs of four columns");
 #pragma unroll
-      for (int fn = 0; fn < TS::FN; ++fn) {
-        const int lcol = wcol0 + fn * 16 + 4 * (lane >> 4);
+        for (int fn = 0; fn < TS::FN; ++fn) {
+          const int lcol = wcol0 + fn * 16 + 4 * (lane >> 4);
 #pragma unroll
-        for (int fm = 0; fm < TS::FM; ++fm) {
-          const int lrow = fm * 16 + (lane & 15);
-          *reinterpret_cast<MC2_LDS f32x4_t*>(smem + lrow * pitch + lcol * 4) = acc[fm][fn];
+          for (int f = 0; f < QR / 16; ++f) {
+            const int lrow = f * 16 + (lane & 15);
+            *reinterpret_cast<MC2_LDS f32x4_t*>(smem + lrow * pitch + lcol * 4) = acc[fm0 + f][fn];
+          }
         }
       }
+    });
+    {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.gsave + (orow0 + q * QR) * p.ldg);
+      constexpr int RW = QR / TS::NW;  // rows loaded per wave
+#pragma unroll
+      for (int j = 0; j < RW; ++j) {
+        const int r = wave * RW + j;
+        const bool ok = col_ok && q * QR + r < nrows;
+        dma16(rs, smem + GB + r * GROW, ok ? static_cast<uint32_t>(r * p.ldg) + coff : kOffNone);
+      }
     }
+    wait_vmcnt0();
     __syncthreads();
-    for (int q = tid; q < HR * CPR; q += TS::NT) {
-      const int r = q / CPR, c8 = q - r * CPR;
-      const int64_t row = half * HR + r;
+    // (not unrolled: the accumulators leave few registers for the LDS values)
+#pragma unroll 2
+    for (int it = tid; it < QR * CPR; it += TS::NT) {
+      const int r = it / CPR, c8 = it - r * CPR;
+      const int64_t row = q * QR + r;
       const int64_t col = ocol0 + c8 * 8;
       if (row >= nrows || col >= p.inter) continue;
       const MC2_LDS float* src = reinterpret_cast<const MC2_LDS float*>(smem + r * pitch + c8 * 32);
-      const char* grow = p.gsave + (orow0 + row) * p.ldg;
-      const u32x4_t gv = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(grow + col * 2));
+      const u32x4_t gv = *reinterpret_cast<const MC2_LDS u32x4_t*>(smem + GB + r * GROW + c8 * 16);
       const u32x4_t uv =
-          __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(grow + (p.inter + col) * 2));
+          *reinterpret_cast<const MC2_LDS u32x4_t*>(smem + GB + r * GROW + TS::BN * 2 + c8 * 16);
       u32x4_t dg, du;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -178,8 +223,6 @@ __device__ __forceinline__ void swiglu_bwd_epilogue(lds_t* smem, const f32x4_t (
   }
 }
 
-// Persistent grouped GEMM: every workgroup derives the tile -> (expert, rows,
-// columns) map from the device-side counts, so the host never reads them.
 // rows [0, BM/2) or [BM/2, BM) of a TS tile
 template <class TS>
 using TileHalf = Tile<TS::BM / 2, TS::BN, TS::WM, TS::WN>;
