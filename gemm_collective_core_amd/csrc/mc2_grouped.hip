@@ -559,10 +559,10 @@ __global__ __launch_bounds__(TS::NT, 1) void wgrad_kernel(WgradArgs p) {
     return;
   }
   const int x = static_cast<int>(blockIdx.x & 7);
-  const int64_t j = blockIdx.x >> 3;
-  // 64-bit division runs on the vector ALU: its results are made uniform again
-  const int64_t sig = uni(j / p.q);
-  const int i = uni(static_cast<int>(j - sig * p.q));
+  const int j = static_cast<int>(blockIdx.x >> 3);
+  // integer division runs on the vector ALU: its results are made uniform again
+  const int sig = uni(j / p.q);
+  const int i = uni(j - sig * p.q);
   if (sig >= uni(s_sstart[El])) return;
   int tm, tn;
   if (p.bm) {
