@@ -144,7 +144,7 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   constexpr int NAR = AK ? 2 * FM : FM;  // A operand reads per k-step (8 bytes each if AK)
   constexpr int NR = NAR + NBR;     // operand reads per wave per k-step
   static_assert(TS::NW == 4 && TS::BN == 256, "four waves, 256-column tiles");
-  static_assert(BT || ES == 2, "row-major B: 16-bit elements");
+  static_assert(!AK || ES == 2, "row-major A: 16-bit elements");
   static_assert(!AK || (!BT && TS::BM == 256), "row-major A: with row-major B, 256-row tiles");
   static_assert(NL <= 63, "vmcnt range of the prologue");
   constexpr int MM = FM * FN;       // MFMA slots per k-step
@@ -216,12 +216,19 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
         l_off[j] = static_cast<uint32_t>((gc - col0) * B.ld + c * 16);
       }
       l_key[j] = c * CE;
-    } else {
+    } else if constexpr (ES == 2) {
       const int o = (NB * wave + (j - NA)) * 1024 + 16 * lane;
       const int kr = o / (TS::BN * 2);
       const int pc = (o - kr * (TS::BN * 2)) >> 4;
       const int ch = (kmaj_unpos16<TS::BN>(pc >> 1, kr) << 1) | (pc & 1);
       l_off[j] = static_cast<uint32_t>(kr * B.ld + colmap(ch * 8) * 2);
+      l_key[j] = kr;
+    } else {
+      // 8-bit: four k rows of 256 bytes per load, 16-byte units swizzled by
+      // kmaj_swz8 (the layout of the eight-wave loop)
+      const int kr = 4 * (NB * wave + (j - NA)) + (lane >> 4);
+      const int ch = (lane & 15) ^ kmaj_swz8(kr);
+      l_off[j] = static_cast<uint32_t>(kr * B.ld + colmap(ch * 16));
       l_key[j] = kr;
     }
   }
@@ -301,13 +308,24 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
   // wcol0 / 16 | (fn ^ swizzle): one address register per fragment, with
   // buffer, k-step and half in the immediate offset.
   uint32_t adT[BT ? 1 : FN];
-  if constexpr (!BT) {
+  if constexpr (!BT && ES == 2) {
     const int j = lane & 15, g = lane >> 4;
     const int swz = (j >> 2) | ((g & 1) << 2);
     const uint32_t base = s0 + kB0 + (g * 8 + (j >> 2)) * (TS::BN * 2) + ((j & 3) << 3);
 #pragma unroll
     for (int fn = 0; fn < FN; ++fn)
       adT[fn] = base + ((((wcol0 >> 4) | (fn ^ swz))) << 5);
+  } else if constexpr (!BT) {
+    // 8-bit row-major B: lane j of group g reads k row 64 k2 + 16 g + 8 h +
+    // (j >> 1) (k-step k2, half h: both in the immediate offset), 16-byte
+    // unit (wcol0 / 16 + fn) ^ kmaj_swz8 of that row, byte 8 (j & 1); the
+    // swizzle depends only on the lane: (j >> 1) | (g & 1) << 3
+    const int j = lane & 15, g = lane >> 4;
+    const int swz = (j >> 1) | ((g & 1) << 3);
+    const uint32_t base = s0 + kB0 + (g * 16 + (j >> 1)) * TS::BN + ((j & 1) << 3);
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      adT[fn] = base + ((((wcol0 >> 4) + fn) ^ swz) << 4);
   }
   // Row-major A: the same with the wave's rows (wrow0 / 16 in {0, 8}) and
   // A's buffers.
@@ -341,11 +359,18 @@ __device__ __forceinline__ void mainloop_w4(lds_t* smem, const char* A, int64_t 
       b.q[i] = lds_rd128_at<i * 16 * kKBytes>(adB[P][K2]);
     } else {
       constexpr int fn = i / 2, h = i % 2;
-      constexpr int off = P * TS::kBBytes + (32 * K2 + 4 * h) * TS::BN * 2;
-      static_assert(off < 65536, "ds_read offset field");
       const uint32_t addr = adT[fn];
-      asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                   : "=v"(b.h[fn][h]) : "v"(addr), "i"(off) : "memory");
+      if constexpr (ES == 2) {
+        constexpr int off = P * TS::kBBytes + (32 * K2 + 4 * h) * TS::BN * 2;
+        static_assert(off < 65536, "ds_read offset field");
+        asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                     : "=v"(b.h[fn][h]) : "v"(addr), "i"(off) : "memory");
+      } else {
+        constexpr int off = P * TS::kBBytes + (64 * K2 + 8 * h) * TS::BN;
+        static_assert(off < 65536, "ds_read offset field");
+        asm volatile("ds_read_b64_tr_b8 %0, %1 offset:%2"
+                     : "=v"(b.h[fn][h]) : "v"(addr), "i"(off) : "memory");
+      }
     }
   };
   auto tie = [&](AOps& a, BOps& b) {

@@ -475,8 +475,8 @@ static hipError_t launch_chunked(const ChunkedArgs& a, int blocks, hipStream_t s
 }
 
 // Instantiated combinations: F16 -> {F16, F32}; BF16 -> {BF16, F32};
-// I8 -> {BF16, F16, F32, I32} (eight-wave tiles, and four-wave 128-row tiles
-// with B given (n, k)).
+// I8 -> {BF16, F16, F32, I32} (eight-wave tiles, and four-wave 128-row
+// tiles).
 template <bool BT, class TS>
 static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArgs& a, int blocks,
                                    hipStream_t s) {
@@ -486,7 +486,7 @@ static hipError_t dispatch_chunked(int in_dtype, int out_dtype, const ChunkedArg
   if (in_dtype == MC2_BF16)
     return out_dtype == MC2_F32 ? launch_chunked<Elem::BF16, BT, TS, Out::F32>(a, blocks, s)
                                 : launch_chunked<Elem::BF16, BT, TS, Out::BF16>(a, blocks, s);
-  if constexpr (TS::NW == 4 && (TS::BM == 256 || !BT)) {
+  if constexpr (TS::NW == 4 && TS::BM == 256) {
     return hipErrorInvalidValue;
   } else {
     switch (out_dtype) {
@@ -611,8 +611,9 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
     a.n_full = static_cast<int>(tiles - rem);
     blocks = tiles + rem;
   }
-  // The four-wave loop runs 16-bit inputs in both B layouts and int8 with B
-  // given (n, k) in 128-row tiles; other int8 tiles run the eight-wave loop.
+  // The four-wave loop runs 16-bit inputs in both B layouts and int8 in
+  // 128-row tiles in both B layouts; int8 256-row tiles run the eight-wave
+  // loop.
   hipError_t e;
   if (x2_trans && es == 1 && tall)
     e = dispatch_chunked<true, TileL>(in_dtype, out_dtype, a, (int)blocks, stream);
@@ -624,7 +625,7 @@ int run_chunked(const void* x1, const void* x2, int64_t m, int64_t k, int64_t n,
              : dispatch_chunked<false, TileWM>(in_dtype, out_dtype, a, (int)blocks, stream);
   else
     e = tall ? dispatch_chunked<false, TileL>(in_dtype, out_dtype, a, (int)blocks, stream)
-             : dispatch_chunked<false, TileM>(in_dtype, out_dtype, a, (int)blocks, stream);
+             : dispatch_chunked<false, TileWM>(in_dtype, out_dtype, a, (int)blocks, stream);
   return e == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 
