@@ -49,6 +49,7 @@ PEAK_HBM = 8000.0    # GB/s, HBM3E (published)
 # the HBM traffic recorded under profiles/ is reported only while their code,
 # comments and blank space aside, is unchanged since the counters were taken.
 KERNEL_SOURCES = ["gemm_collective_core_amd/csrc/gemm_core.hpp",
+                  "gemm_collective_core_amd/csrc/gemm_core_w4.hpp",
                   "gemm_collective_core_amd/csrc/mc2_tiles.hpp",
                   "gemm_collective_core_amd/csrc/mc2_chunked.hpp",
                   "gemm_collective_core_amd/csrc/mc2_gemm.hip",
