@@ -23,19 +23,54 @@ __global__ __launch_bounds__(kMoeThreads) void fill_i32_kernel(int32_t* p, int64
 }
 
 // ---------------------------------------------------------------- histc
+//
+// A block counts chunks of kHistcChunk ids: every thread issues its four
+// 16-byte loads (16 ids) before it counts any, so a chunk costs one memory
+// latency, and adds them to the block's LDS histogram. The block then adds its
+// non-zero counters to `counts` (cleared by the fill kernel launched before).
+// The global atomics, E per block on the same E words, are what costs: the
+// large chunk keeps the block count, and with it their number, low.
+
+constexpr int kHistcLoads = 4;                              // 16-byte loads per thread
+constexpr int kHistcChunk = kMoeThreads * kHistcLoads * 4;  // 4096 ids per chunk
 
 __global__ __launch_bounds__(kMoeThreads) void histc_kernel(const int32_t* __restrict__ sel,
-                                                            int64_t n, int E, int32_t* counts,
-                                                            int32_t* dev_err) {
+                                                            int64_t n, int E, int vec_ok,
+                                                            int32_t* counts, int32_t* dev_err) {
   __shared__ int h[kMaxExperts];
   for (int e = threadIdx.x; e < E; e += kMoeThreads) h[e] = 0;
   __syncthreads();
   bool bad = false;
-  for (int64_t i = blockIdx.x * (int64_t)kMoeThreads + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * kMoeThreads) {
-    const int32_t v = sel[i];
-    if (v >= 0 && v < E) atomicAdd(&h[v], 1);
-    else bad = true;
+  for (int64_t c0 = (int64_t)blockIdx.x * kHistcChunk; c0 < n;
+       c0 += (int64_t)gridDim.x * kHistcChunk) {
+    int v[kHistcLoads * 4];
+    const bool full = vec_ok && c0 + kHistcChunk <= n;
+    if (full) {
+      // load j of the block covers 1024 consecutive ids; lane order within a
+      // wave is contiguous, so each wave load reads 1 KiB in one sweep
+      const i32x4_t* p = reinterpret_cast<const i32x4_t*>(sel + c0);
+#pragma unroll
+      for (int j = 0; j < kHistcLoads; ++j) {
+        const i32x4_t q = p[j * kMoeThreads + threadIdx.x];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[j * 4 + c] = q[c];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kHistcLoads * 4; ++j) {
+        const int64_t i = c0 + (int64_t)j * kMoeThreads + threadIdx.x;
+        v[j] = i < n ? sel[i] : 0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kHistcLoads * 4; ++j) {
+      // ids outside [0, E) are reported and not counted; a lane past the end
+      // has nothing to count
+      const bool in = full || (int64_t)j * kMoeThreads + threadIdx.x < n - c0;
+      const int id = v[j];
+      if (in && id >= 0 && id < E) atomicAdd(&h[id], 1);
+      else if (in) bad = true;
+    }
   }
   if (bad) atomic_or_err(dev_err, MC2_DEVERR_EXPERT_ID);
   __syncthreads();
@@ -319,9 +354,12 @@ extern "C" int mc2_moe_histc(const int32_t* sel, int64_t n_ids, int num_experts,
   if (n_ids < 0 || num_experts < 1 || num_experts > kMaxExperts) return MC2_ERR_SHAPE;
   hipLaunchKernelGGL(fill_i32_kernel, dim3(grid_for(num_experts, 1, 64)), dim3(kMoeThreads), 0,
                      stream, counts, (int64_t)num_experts, 0);
-  if (n_ids > 0)
-    hipLaunchKernelGGL(histc_kernel, dim3(grid_for(n_ids, 4, 1024)), dim3(kMoeThreads), 0, stream,
-                       sel, n_ids, num_experts, counts, dev_err);
+  if (n_ids > 0) {
+    const int vec_ok = (reinterpret_cast<uintptr_t>(sel) & 15) == 0;
+    hipLaunchKernelGGL(histc_kernel, dim3(grid_for(n_ids, kHistcChunk / kMoeThreads, 1024)),
+                       dim3(kMoeThreads), 0, stream, sel, n_ids, num_experts, vec_ok, counts,
+                       dev_err);
+  }
   return hipGetLastError() == hipSuccess ? MC2_OK : MC2_ERR_HIP;
 }
 

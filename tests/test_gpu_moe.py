@@ -35,6 +35,30 @@ def test_histc_bit_exact_and_invalid_ids():
     assert err.item() & mc2.MC2_DEVERR_EXPERT_ID
 
 
+@pytest.mark.parametrize("n,E,offset", [
+    (3 * 4096 + 77, 128, 0),    # whole 4096-id chunks (16-byte loads), then a ragged chunk
+    (3 * 4096 + 77, 128, 1),    # ids not 16-byte aligned: element loads throughout
+    (1029 * 4096 + 3, 128, 0),  # more chunks than blocks: blocks take a second chunk
+    (8192, 1024, 0), (4096, 1, 0), (1, 5, 0), (4095, 3, 3)])
+def test_histc_chunks_alignment_and_grid_stride(n, E, offset):
+    sel = wl.expert_ids(77 + n % 1000, n, E)
+    base = torch.zeros(n + offset, dtype=torch.int32, device="cuda")
+    dsel = base[offset:]
+    dsel.copy_(torch.from_numpy(sel))
+    err = _err()
+    counts = mc2.mc2_moe_histc(dsel, E, dev_err=err)
+    np.testing.assert_array_equal(counts.cpu().numpy(), om.histc(sel, E))
+    assert err.item() == 0  # lanes past the end are never reported as invalid ids
+    # invalid ids in the first (whole) chunk and in the last one
+    bad = sel.copy()
+    for pos, v in ((0, E), (5, -1), (4000, 2**31 - 1), (n - 1, -2**31), (n // 2, E + 1)):
+        bad[min(pos, n - 1)] = v
+    dsel.copy_(torch.from_numpy(bad))
+    counts = mc2.mc2_moe_histc(dsel, E, counts=counts, dev_err=err)
+    np.testing.assert_array_equal(counts.cpu().numpy(), om.histc(bad, E))
+    assert err.item() & mc2.MC2_DEVERR_EXPERT_ID
+
+
 @pytest.mark.parametrize("T,K,E", [(700, 4, 32), (33, 8, 128), (5, 1, 3), (64, 64, 1024),
                                    (129, 3, 17)])
 def test_permute_bit_exact(T, K, E):

@@ -187,6 +187,17 @@ def router(logits: np.ndarray, expert_bias: np.ndarray, topk: int):
     return np.ascontiguousarray(sel), np.ascontiguousarray(probs)
 
 
+def expert_ids(seed, n, num_experts):
+    """n expert ids, int32, drawn independently from a skewed distribution:
+    p(e) proportional to exp(b_e) with b N(0, 0.5) (the router's expert bias
+    without the per-token logits). Draw order: b (E), then the n ids."""
+    rng = np.random.default_rng(seed)
+    b = rng.standard_normal(size=(num_experts,)) * 0.5
+    p = np.exp(b - b.max())
+    p /= p.sum()
+    return rng.choice(num_experts, size=n, p=p).astype(np.int32)
+
+
 def moe_inputs(seed=1004, tokens=32768, hidden=2048, num_experts=128, topk=8,
                local_experts=16, inter=768, x_std=1.0, w_std=0.02):
     """MoE EP local share, bf16.
