@@ -267,52 +267,56 @@ __global__ __launch_bounds__(kMoeThreads) void permute_scatter_kernel(
 
 // ---------------------------------------------------------------- unpermute
 
-// One wave per token; lanes own 16-byte column chunks (8 bf16). Rows of up to
-// 8 slots are loaded before they are accumulated so that their loads overlap.
-// Every y row is read once and every output row written once: both go
-// non-temporal.
+// One wave per token; lanes own 16-byte column chunks (8 bf16), four per lane
+// in a pass of 256 chunks (the whole row for H <= 2048). The slot indices and
+// weights of a group of 8 slots are loaded once per pass by lanes 0-7 and
+// broadcast, so the row addresses are wave-uniform; the 8 rows' loads of a
+// pass are all issued before any is accumulated. Every y row is read once and
+// every output row written once: both go non-temporal. Sums run in fp32 with k
+// ascending, one fma per slot (an invalid slot adds 0 * 0).
 __global__ __launch_bounds__(kMoeThreads) void unpermute_kernel(
     const uint16_t* __restrict__ y, int64_t y_rows, const int32_t* __restrict__ idx,
     const float* __restrict__ probs, int64_t T, int K, int64_t H, uint16_t* __restrict__ out,
     int32_t* dev_err) {
+  constexpr int kC = 4;  // 16-byte chunks per lane per pass
   const int lane = threadIdx.x & 63;
   const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const int64_t CR = H / 8;
   bool bad = false;
-  for (int64_t base = 0; base < CR; base += 128) {
-    float acc[2][8];
+  for (int64_t base = 0; base < CR; base += 64 * kC) {
+    float acc[kC][8];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int c = 0; c < kC; ++c)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[c][i] = 0.f;
     for (int k0 = 0; k0 < K; k0 += 8) {
-      uint4 v[8][2];
+      int p_l = -1;
+      float w_l = 0.f;
+      if (lane < 8 && k0 + lane < K) {
+        p_l = idx[t * K + k0 + lane];
+        w_l = probs[t * K + k0 + lane];
+        if (p_l >= y_rows) { bad = true; p_l = -1; }
+        if (p_l < 0) w_l = 0.f;
+      }
+      uint4 v[8][kC];
       float w[8];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const int k = k0 + kk;
-        int p = -1;
-        w[kk] = 0.f;
-        if (k < K) {
-          p = idx[t * K + k];
-          w[kk] = probs[t * K + k];
-          if (p >= y_rows) { bad = true; p = -1; }
-        }
+        const int p = __builtin_amdgcn_readlane(p_l, kk);
+        w[kk] = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), kk));
+        const u32x4_t* row = reinterpret_cast<const u32x4_t*>(y + (int64_t)(p < 0 ? 0 : p) * H);
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < kC; ++c) {
           const int64_t j = base + c * 64 + lane;
-          v[kk][c] = (p >= 0 && j < CR)
-                         ? bit_cast<uint4>(__builtin_nontemporal_load(
-                               reinterpret_cast<const u32x4_t*>(y + (int64_t)p * H) + j))
-                         : zero4();
+          v[kk][c] = (p >= 0 && j < CR) ? bit_cast<uint4>(__builtin_nontemporal_load(row + j))
+                                        : zero4();
         }
-        if (p < 0) w[kk] = 0.f;
       }
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < kC; ++c) {
           const uint32_t d[4] = {v[kk][c].x, v[kk][c].y, v[kk][c].z, v[kk][c].w};
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
@@ -323,7 +327,7 @@ __global__ __launch_bounds__(kMoeThreads) void unpermute_kernel(
       }
     }
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < kC; ++c) {
       const int64_t j = base + c * 64 + lane;
       if (j < CR) {
         uint4 o;

@@ -117,6 +117,23 @@ def test_unpermute_parity_with_standins():
     assert_tol(to_f64(out), ref, "unpermute")
 
 
+@pytest.mark.parametrize("T,K,H", [(37, 13, 2312), (50, 64, 72), (9, 9, 4096)])
+def test_unpermute_slot_groups_and_column_passes(T, K, H):
+    """More than 8 slots per token (several groups of 8, the last one ragged)
+    and rows of more than 2048 columns (several column passes, the last one
+    ragged), with slots that hold no row."""
+    rng = np.random.default_rng(T * K + H)
+    y = wl.combine_standins(37, T * K, H, std=1.0)
+    idx = rng.permutation(T * K).astype(np.int32)
+    idx[rng.choice(T * K, size=max(1, T * K // 10), replace=False)] = -1
+    probs = rng.uniform(0, 1, (T, K)).astype(np.float32)
+    err = _err()
+    out = mc2.mc2_moe_unpermute(to_dev(y, "bf16"), to_dev(idx), to_dev(probs), dev_err=err)
+    ref = om.unpermute(on.decode(y, "bf16"), idx, probs, T, K)
+    assert_tol(to_f64(out), ref, "unpermute")
+    assert err.item() == 0
+
+
 def test_unpermute_out_of_range_index_flagged():
     T, K, H = 4, 2, 8
     y = wl.combine_standins(36, 8, H)
