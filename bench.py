@@ -502,6 +502,22 @@ def main():
                                               ("fc1", f_disp), ("fc2", f_comb),
                                               ("unpermute", f_unperm))}
         t_all = measure(lambda: [f() for f in (f_histc, f_perm, f_disp, f_comb, f_unperm)])
+        # histc alone is two launches of a few microseconds: called one by one
+        # from Python they run at the host's launch rate, so it is also timed
+        # as a replayed graph of 20 calls (the library records no memset)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            f_histc()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g_histc = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_histc):
+            for _ in range(20):
+                f_histc()
+        t_histc_graph = measure(g_histc.replay)
+        torch.cuda.synchronize()
+        assert err.item() == 0
         fl1 = 2.0 * n_loc * H * 2 * I
         fl2 = 2.0 * n_loc * I * H
         perm_bytes = T * H * 2 + T * K * 4 + T * K * H * 2 + 2 * T * K * 4
@@ -510,6 +526,7 @@ def main():
         rows["c4_moe_ep_local"] = {
             "n_loc": n_loc, "ms_step": t_all[0], "ms_step_median": t_all[1],
             "histc_us": t["histc"][0] * 1e3,
+            "histc_us_graph": t_histc_graph[0] / 20 * 1e3,
             "permute_us": t["permute"][0] * 1e3, "permute_us_median": t["permute"][1] * 1e3,
             "permute_GB/s": perm_bytes / t["permute"][0] / 1e6,
             "permute_frac_hbm": perm_bytes / t["permute"][0] / 1e6 / PEAK_HBM,
