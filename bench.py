@@ -10,11 +10,15 @@ flags, each weight held as an (n, k) Linear weight and passed transposed
 
 Before the timed steps the headline runs untimed for a fixed settle time
 (--settle seconds, default 2) so that the clocks have left their ramp; then
---warmup untimed steps and exactly --steps timed steps, each bracketed by HIP
-events on the launch stream (mean and median are reported). The same JSON
-line carries the other hot-path rows (the AllGatherMatmul and int8 shares,
-the MoE expert-parallel local path and its backward, MatmulAllReduce, the
-split granularity), each timed over at least 200 ms with its mean and median;
+--warmup untimed steps and exactly --steps timed steps, run back to back
+between two HIP events on the launch stream: their mean is `ms_per_step`.
+A second pass of --steps steps brackets every step and every launch with
+events for the median and the split between the two launches (an event
+between launches leaves the GPU idle for a few microseconds, so that pass is
+not used for the mean). The same JSON line carries the other hot-path rows
+(the AllGatherMatmul and int8 shares, the MoE expert-parallel local path and
+its backward, MatmulAllReduce, the split granularity), each timed the same
+way over at least 200 ms of calls, with its mean and median;
 the roofline of the headline kernel; the shader clock sampled while it ran;
 and the CPU oracle timed on a bounded sample of the headline workload.
 
@@ -216,9 +220,12 @@ def main():
         return torch.cuda.Event(enable_timing=True)
 
     def measure(fn, min_ms=200.0, warmup=10, min_iters=10, max_iters=5000):
-        """Mean and median milliseconds per call of fn(), over at least
-        `min_ms` of timed calls, each bracketed by HIP events on the current
-        stream (the stream every entry point launches on)."""
+        """Mean and median milliseconds per call of fn(), on the current
+        stream (the stream every entry point launches on). The mean is over at
+        least `min_ms` of calls run back to back between two HIP events; the
+        median comes from a second pass of as many calls, each bracketed by
+        events (which leave the GPU idle for a few microseconds between calls,
+        so that pass does not give the mean)."""
         for _ in range(warmup):
             fn()
         torch.cuda.synchronize()
@@ -230,6 +237,12 @@ def main():
         torch.cuda.synchronize()
         est = max(a.elapsed_time(b) / 3, 1e-3)
         n = int(min(max(min_iters, np.ceil(min_ms / est)), max_iters))
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        mean = a.elapsed_time(b) / n
         evs = [ev() for _ in range(n + 1)]
         evs[0].record()
         for i in range(n):
@@ -237,7 +250,7 @@ def main():
             evs[i + 1].record()
         torch.cuda.synchronize()
         per = [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
-        return evs[0].elapsed_time(evs[n]) / n, float(np.median(per)), n
+        return mean, float(np.median(per)), n
 
     if args.calib_copy:
         n = 1 << 30
@@ -312,21 +325,30 @@ def main():
             step()
         torch.cuda.synchronize()
         K = args.steps
+        # the timed steps, back to back between two events
+        first, last = ev(), ev()
+        t0 = time.perf_counter()
+        first.record()
+        for i in range(K):
+            step()
+        last.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        assert fl_a.cpu().tolist() == [epoch[0]] * W and fl_b.cpu().tolist() == [epoch[0]] * W
+        ms = first.elapsed_time(last) / K
+        # a second pass with every step and launch bracketed: median, launch split
         starts = [ev() for _ in range(K + 1)]
         mids = [ev() for _ in range(K)]
-        t0 = time.perf_counter()
         starts[0].record()
         for i in range(K):
             step(mids[i])
             starts[i + 1].record()
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
         clock.stop()
         assert fl_a.cpu().tolist() == [epoch[0]] * W and fl_b.cpu().tolist() == [epoch[0]] * W
         per_step = [starts[i].elapsed_time(starts[i + 1]) for i in range(K)]
         t_a = [starts[i].elapsed_time(mids[i]) for i in range(K)]
         t_b = [mids[i].elapsed_time(starts[i + 1]) for i in range(K)]
-        ms = starts[0].elapsed_time(starts[K]) / K
         tf = (FLOP_A + FLOP_B) / ms / 1e9
         ka, kb = float(np.mean(t_a)), float(np.mean(t_b))
         headline = {"ms": ms, "ms_median": float(np.median(per_step)), "tflops": tf,
